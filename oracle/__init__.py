@@ -1,0 +1,19 @@
+"""CPU oracle (FP64) for the paged KV cache decode path.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py``; never by the library in ``paged_kv_cache_pages_amd``.
+"""
+
+from .paged_oracle import (  # noqa: F401
+    attend_one,
+    attend_one_online,
+    bf16_bits_to_f64,
+    bf16_round_nearest_even,
+    gather_context,
+    kv_append,
+    kv_head_of,
+    locate_slot,
+    merge_states,
+    paged_decode_attention,
+    softmax_two_pass,
+)
