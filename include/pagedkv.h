@@ -1,0 +1,181 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv: the decode-step hot path of a paged BF16 KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Two calls carry the method: pkv_kv_append writes each sequence's new K/V row into its page,
+ * and pkv_paged_decode_attention streams each sequence's pages with grouped-query attention and
+ * an FP32 online softmax.  The rest are helpers (planning, workspace size, host-side
+ * validation, status strings).
+ *
+ * Conventions for every call:
+ *   - Pointers documented as "device" must point to GPU memory of the current HIP device;
+ *     "host" pointers to ordinary CPU memory.  The caller owns every buffer; the library
+ *     allocates no device memory, keeps no per-call state and is reentrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is only
+ *     enqueued; nothing synchronises with the host unless debug validation is on (below).
+ *     Ordering between calls comes from stream order.
+ *   - BF16 values travel as their 16-bit patterns (uint16_t storage).  Every device buffer
+ *     must be 16-byte aligned (the kernels move 16-byte vectors).
+ *   - Return value: PKV_OK, or the first error found by the synchronous host checks.  No
+ *     kernel is launched when a check fails.  Kernels never read or write out of bounds: a
+ *     block-table entry outside [0, num_pages), a position outside the table, or a context
+ *     length outside [0, 16 * max_blocks_per_seq] is never dereferenced; append skips that
+ *     row and attention writes zeros for that sequence.
+ *   - Environment PKV_DEBUG_VALIDATE=1 makes both calls copy the block tables, positions and
+ *     context lengths to the host (synchronously) and return PKV_ERR_VALIDATION instead of
+ *     launching when any of them is out of range, when a table entry needed by the step is -1,
+ *     or (append) when two sequences target the same (page, slot).
+ *
+ * Page pool layout ("[page][kv_head][token][dim]"): K and V live in two separate buffers, each
+ * bf16[num_pages][num_kv_heads][block_size][head_dim], so the 16 tokens of one KV head in one
+ * page are one contiguous 2 KiB run (block_size 16, head_dim 64).
+ *
+ * Supported geometry (anything else returns PKV_ERR_UNSUPPORTED): block_size 16, head_dim 64,
+ * num_q_heads == 4 * num_kv_heads.  These are the Llama-3.2-1B decode constants of the pages:
+ * 16-token pages (jaehun.me, code-series index, part 6 "Splitting the KV cache into 16-token
+ * blocks"), 32 query heads over 8 KV heads with consecutive groups of four and head_dim 64
+ * (jaehun.me, "The prefill path", section "Per-head attention scores and GQA").
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL                                    */
+  PKV_ERR_SHAPE = 2,       /* a size is negative/zero where it must be positive, or scale  */
+                           /* is not a positive finite number                               */
+  PKV_ERR_UNSUPPORTED = 3, /* geometry outside the compiled kernels (see above)             */
+  PKV_ERR_WORKSPACE = 4,   /* the chosen split needs more workspace than was passed         */
+  PKV_ERR_VALIDATION = 5,  /* debug validation rejected the data (PKV_DEBUG_VALIDATE=1)     */
+  PKV_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed                    */
+  PKV_ERR_ALIGNMENT = 7    /* a device buffer is not 16-byte aligned                        */
+} pkv_status;
+
+typedef enum {
+  PKV_OUT_BF16 = 0, /* output stored as BF16, rounded to nearest even from the FP32 result */
+  PKV_OUT_F32 = 1   /* output stored as FP32 (the pre-rounding value, used for parity)     */
+} pkv_out_dtype;
+
+/* The shared page pool.  k_pool / v_pool: device, bf16[num_pages][num_kv_heads][block_size]
+ * [head_dim] each. */
+typedef struct {
+  void *k_pool;
+  void *v_pool;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+} pkv_pool;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *pkv_status_string(pkv_status status);
+
+/* PKV_ABI_VERSION of the built library. */
+int32_t pkv_abi_version(void);
+
+/*
+ * kv_append(pool, block_tables, positions, k_new, v_new)
+ *
+ * Decode-side KV write: for every sequence b and KV head g, copy k_new[b][g][:] into
+ * K[page][g][slot][:] and v_new[b][g][:] into V[page][g][slot][:], where
+ * page = block_tables[b * max_blocks_per_seq + positions[b] / 16] and slot = positions[b] % 16.
+ * The pages describe this step as decode appending one new token at its absolute (RoPE)
+ * position into the shared BF16 page pool (news.t0.vc/TXJZ, "What works so far"), with the
+ * page found through the per-sequence block table (jaehun.me, "The prefill path", section
+ * "Distributing K/V into paged blocks").  The copy is bit-exact.
+ *
+ *   pool                host struct; its k_pool / v_pool are device buffers (modified)
+ *   block_tables        device int32[batch][max_blocks_per_seq]; the entry for block
+ *                       positions[b] / 16 must already hold a page (the host allocator
+ *                       assigns a fresh page when positions[b] % 16 == 0); other entries unused
+ *   positions           device int32[batch], absolute position of the new token
+ *   k_new, v_new        device bf16[batch][num_kv_heads][head_dim]
+ *   batch               >= 0 (0 is a no-op)
+ * Preconditions: targets are distinct (page, slot) pairs; otherwise which row lands is
+ * unspecified.  Rows with an out-of-range position or page id are skipped.
+ */
+pkv_status pkv_kv_append(const pkv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                         const int32_t *positions, const void *k_new, const void *v_new, int32_t batch,
+                         void *stream);
+
+/*
+ * paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out)
+ *
+ * For every sequence b, query head h (KV head g = h / 4) and dim d:
+ *   s_t = scale * sum_d q[b][h][d] * K[page(t)][g][t % 16][d]          for t < L = context_lens[b]
+ *   out[b][h][:] = sum_t softmax(s)_t * V[page(t)][g][t % 16][:]
+ * with page(t) = block_tables[b * max_blocks_per_seq + t / 16].  The pages' decode attention
+ * streams each sequence's cached pages per query head and accumulates weighted values with an
+ * FP32 online softmax, gathering no contiguous prefix and storing no scores (news.t0.vc/TXJZ,
+ * "What works so far"); the online-softmax merge of partial (max, sum) pairs is the rule of
+ * jaehun.me, "The prefill path", section "causalMask and online softmax".  Inputs are BF16,
+ * all arithmetic is FP32, the output is FP32 or BF16 (round to nearest even).
+ *
+ *   q                 device bf16[batch][num_q_heads][head_dim]
+ *   k_pool, v_pool    device bf16[num_pages][num_kv_heads][block_size][head_dim]
+ *   block_tables      device int32[batch][max_blocks_per_seq]
+ *   context_lens      device int32[batch]; tokens attended, including the one just appended;
+ *                     0 gives an all-zero output row
+ *   out               device, bf16 or f32 [batch][num_q_heads][head_dim] per out_dtype
+ *   scale             positive finite score scale (1/sqrt(head_dim) = 0.125 for Llama)
+ *   partition_pages   pages per context partition.  <= 0: choose automatically with
+ *                     pkv_plan_partition_pages for the current device.  When a sequence's
+ *                     pages are cut into several partitions, each partition produces a
+ *                     (max, sum, partial output) triple per query head in `workspace` and a
+ *                     second kernel merges them; >= max_blocks_per_seq never splits.
+ *   workspace         device scratch of at least pkv_decode_workspace_bytes(...) bytes for the
+ *                     resolved partition size (may be NULL when that is 0).  Contents on entry
+ *                     are ignored; on return they are unspecified.
+ */
+pkv_status pkv_paged_decode_attention(const void *q, const void *k_pool, const void *v_pool, int32_t num_pages,
+                                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t *context_lens, void *out, pkv_out_dtype out_dtype,
+                                      int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, float scale, int32_t partition_pages, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/*
+ * Pages per partition chosen when partition_pages <= 0.  Pure function (no GPU needed):
+ * no split when batch * num_kv_heads workgroups already cover the device, otherwise the
+ * smallest multiple of 4 pages (at least 4) that yields about 4 workgroups per compute unit.
+ * Returns a value >= max_blocks_per_seq when no split is needed; -1 on bad arguments.
+ */
+int32_t pkv_plan_partition_pages(int32_t batch, int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t num_cus);
+
+/* Workspace bytes needed for the given (resolved, positive) partition size; 0 without a split.
+ * Returns 0 on bad arguments. */
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                  int32_t partition_pages);
+
+/* Compute units of the current HIP device, or -1 when no device is available. */
+int32_t pkv_device_cu_count(void);
+
+/*
+ * Host-side data validation (plain C++, no GPU needed; also what PKV_DEBUG_VALIDATE runs).
+ * All pointers are host pointers.  On failure *bad_row (if not NULL) receives the offending
+ * batch row; on success it receives -1.
+ *
+ * Append: every position is in [0, 16 * max_blocks_per_seq), the entry for block
+ * positions[b] / 16 is in [0, num_pages), and no two rows target the same (page, slot).
+ * Decode: every context length is in [0, 16 * max_blocks_per_seq] and the first
+ * ceil(L / 16) entries of the row are in [0, num_pages).
+ */
+pkv_status pkv_validate_append_host(const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *positions,
+                                    int32_t batch, int32_t num_pages, int32_t *bad_row);
+pkv_status pkv_validate_decode_host(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, int32_t batch, int32_t num_pages, int32_t *bad_row);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

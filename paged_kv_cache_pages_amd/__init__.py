@@ -1,0 +1,25 @@
+"""Paged KV cache decode step for AMD Instinct MI355X (gfx950).
+
+``kv_append`` and ``paged_decode_attention`` are thin bindings of the C ABI in
+``include/pagedkv.h``; the work runs in hand-written HIP kernels (``csrc/``).  PyTorch supplies
+device memory and the current stream only.
+"""
+
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    PKV_OUT_BF16,
+    PKV_OUT_F32,
+    SIGNATURES,
+    STATUS_NAMES,
+    PagedKVError,
+    Pool,
+    cu_count,
+    decode_workspace_bytes,
+    kv_append,
+    library,
+    paged_decode_attention,
+    plan_partition_pages,
+    require_library,
+    validate_append_host,
+    validate_decode_host,
+)

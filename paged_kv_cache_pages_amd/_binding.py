@@ -1,0 +1,255 @@
+"""ctypes binding of libpagedkv: argument marshalling only.
+
+Every step of the decode path runs in the HIP kernels of ``libpagedkv.so``; this module checks
+tensor dtypes, shapes, devices and contiguity, takes raw pointers and the current HIP stream from
+PyTorch, and calls the C ABI declared in ``include/pagedkv.h``.  There is no fallback: without the
+built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpagedkv.so")
+
+PKV_OK = 0
+PKV_OUT_BF16 = 0
+PKV_OUT_F32 = 1
+STATUS_NAMES = {
+    0: "PKV_OK",
+    1: "PKV_ERR_NULL",
+    2: "PKV_ERR_SHAPE",
+    3: "PKV_ERR_UNSUPPORTED",
+    4: "PKV_ERR_WORKSPACE",
+    5: "PKV_ERR_VALIDATION",
+    6: "PKV_ERR_HIP",
+    7: "PKV_ERR_ALIGNMENT",
+}
+
+# Every symbol the header declares, with its ctypes signature.
+_c_int32 = ctypes.c_int32
+_c_size = ctypes.c_size_t
+_vp = ctypes.c_void_p
+
+
+class Pool(ctypes.Structure):
+    _fields_ = [
+        ("k_pool", _vp),
+        ("v_pool", _vp),
+        ("num_pages", _c_int32),
+        ("num_kv_heads", _c_int32),
+        ("head_dim", _c_int32),
+        ("block_size", _c_int32),
+    ]
+
+
+SIGNATURES = {
+    "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_abi_version": (_c_int32, []),
+    "pkv_kv_append": (ctypes.c_int, [ctypes.POINTER(Pool), _vp, _c_int32, _vp, _vp, _vp, _c_int32, _vp]),
+    "pkv_paged_decode_attention": (
+        ctypes.c_int,
+        [_vp, _vp, _vp, _c_int32, _vp, _c_int32, _vp, _vp, ctypes.c_int, _c_int32, _c_int32, _c_int32, _c_int32,
+         _c_int32, ctypes.c_float, _c_int32, _vp, _c_size, _vp],
+    ),
+    "pkv_plan_partition_pages": (_c_int32, [_c_int32, _c_int32, _c_int32, _c_int32]),
+    "pkv_decode_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
+    "pkv_device_cu_count": (_c_int32, []),
+    "pkv_validate_append_host": (ctypes.c_int, [_vp, _c_int32, _vp, _c_int32, _c_int32, _vp]),
+    "pkv_validate_decode_host": (ctypes.c_int, [_vp, _c_int32, _vp, _c_int32, _c_int32, _vp]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        name = STATUS_NAMES.get(status, str(status))
+        detail = library().pkv_status_string(status).decode()
+        super().__init__(f"{call} failed: {name} ({detail})")
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libpagedkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_pages_amd._build` "
+                    "(there is no CPU fallback)"
+                )
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def require_library() -> None:
+    library()
+
+
+def _check(call: str, status: int) -> None:
+    if status != PKV_OK:
+        raise PagedKVError(call, status)
+
+
+# ---------------------------------------------------------------------------------------------
+# tensor helpers (torch is imported lazily so that host-only users need not load it)
+# ---------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dev_tensor(name, t, dtype, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got shape {tuple(t.shape)})")
+    return t
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def cu_count() -> int:
+    n = library().pkv_device_cu_count()
+    if n <= 0:
+        raise RuntimeError("no HIP device available")
+    return int(n)
+
+
+def plan_partition_pages(batch: int, num_kv_heads: int, max_blocks_per_seq: int, num_cus: int | None = None) -> int:
+    cus = cu_count() if num_cus is None else int(num_cus)
+    r = library().pkv_plan_partition_pages(batch, num_kv_heads, max_blocks_per_seq, cus)
+    if r <= 0:
+        raise ValueError("invalid planning arguments")
+    return int(r)
+
+
+def decode_workspace_bytes(batch: int, num_q_heads: int, max_blocks_per_seq: int, partition_pages: int) -> int:
+    return int(library().pkv_decode_workspace_bytes(batch, num_q_heads, max_blocks_per_seq, partition_pages))
+
+
+# ---------------------------------------------------------------------------------------------
+# the two method calls
+# ---------------------------------------------------------------------------------------------
+
+def kv_append(k_pool, v_pool, block_tables, positions, k_new, v_new, stream=None) -> None:
+    """Write k_new/v_new [B][Hkv][D] into slot pos % 16 of page block_tables[b][pos // 16]."""
+    torch = _torch()
+    _dev_tensor("k_pool", k_pool, torch.bfloat16, 4)
+    _dev_tensor("v_pool", v_pool, torch.bfloat16, 4)
+    _dev_tensor("block_tables", block_tables, torch.int32, 2)
+    _dev_tensor("positions", positions, torch.int32, 1)
+    _dev_tensor("k_new", k_new, torch.bfloat16, 3)
+    _dev_tensor("v_new", v_new, torch.bfloat16, 3)
+    num_pages, hkv, block, dim = k_pool.shape
+    if tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_pool and v_pool shapes differ")
+    batch = positions.shape[0]
+    if block_tables.shape[0] != batch or tuple(k_new.shape) != (batch, hkv, dim) or k_new.shape != v_new.shape:
+        raise ValueError("inconsistent batch / head shapes")
+    pool = Pool(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, hkv, dim, block)
+    st = library().pkv_kv_append(
+        ctypes.byref(pool), block_tables.data_ptr(), block_tables.shape[1], positions.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), batch, _stream_handle(stream),
+    )
+    _check("pkv_kv_append", st)
+
+
+def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=None, *, out_dtype=None, scale=None,
+                           partition_pages: int = 0, workspace=None, stream=None):
+    """Decode attention of q [B][Hq][D] over each sequence's pages; returns out [B][Hq][D].
+
+    ``out_dtype`` is torch.bfloat16 (default) or torch.float32; ``scale`` defaults to
+    1/sqrt(head_dim).  ``partition_pages`` <= 0 lets the library plan the context split; the
+    partial-result workspace is allocated here through torch when none is passed.
+    """
+    torch = _torch()
+    _dev_tensor("q", q, torch.bfloat16, 3)
+    _dev_tensor("k_pool", k_pool, torch.bfloat16, 4)
+    _dev_tensor("v_pool", v_pool, torch.bfloat16, 4)
+    _dev_tensor("block_tables", block_tables, torch.int32, 2)
+    _dev_tensor("context_lens", context_lens, torch.int32, 1)
+    batch, hq, dim = q.shape
+    num_pages, hkv, block, _ = k_pool.shape
+    if tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_pool and v_pool shapes differ")
+    if block_tables.shape[0] != batch or context_lens.shape[0] != batch:
+        raise ValueError("block_tables / context_lens batch differs from q")
+    max_blocks = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((batch, hq, dim), dtype=out_dtype or torch.bfloat16, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _dev_tensor("out", out, out.dtype, 3)
+    if tuple(out.shape) != (batch, hq, dim):
+        raise ValueError("out shape differs from q")
+    if scale is None:
+        scale = 1.0 / float(dim) ** 0.5
+    pp = int(partition_pages)
+    if pp <= 0:
+        pp = plan_partition_pages(batch, hkv, max_blocks)
+    need = decode_workspace_bytes(batch, hq, max_blocks, pp)
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _dev_tensor("workspace", workspace, workspace.dtype)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = library().pkv_paged_decode_attention(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), num_pages, block_tables.data_ptr(), max_blocks,
+        context_lens.data_ptr(), out.data_ptr(), PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32,
+        batch, hq, hkv, dim, block, float(scale), pp, ws_ptr, ws_bytes, _stream_handle(stream),
+    )
+    _check("pkv_paged_decode_attention", st)
+    return out
+
+
+def validate_append_host(block_tables, positions, num_pages: int):
+    """Host-side append validation on numpy int32 arrays: (status, bad_row)."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    bad = ctypes.c_int32(-2)
+    st = library().pkv_validate_append_host(
+        bt.ctypes.data, bt.shape[1] if bt.ndim == 2 else 0, pos.ctypes.data, pos.shape[0], num_pages, ctypes.byref(bad)
+    )
+    return int(st), int(bad.value)
+
+
+def validate_decode_host(block_tables, context_lens, num_pages: int):
+    """Host-side decode validation on numpy int32 arrays: (status, bad_row)."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    bad = ctypes.c_int32(-2)
+    st = library().pkv_validate_decode_host(
+        bt.ctypes.data, bt.shape[1] if bt.ndim == 2 else 0, lens.ctypes.data, lens.shape[0], num_pages, ctypes.byref(bad)
+    )
+    return int(st), int(bad.value)

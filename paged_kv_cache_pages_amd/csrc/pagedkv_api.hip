@@ -1,0 +1,189 @@
+// C ABI of libpagedkv: synchronous host checks, optional debug validation, kernel dispatch.
+// The two method calls follow the problem statement of news.t0.vc/TXJZ ("What works so far":
+// decode appends each new token at its absolute position into a shared BF16 page pool through a
+// per-sequence block table, and decode attention streams each sequence's pages with an FP32
+// online softmax).  Argument meaning, layout and error behaviour are documented in pagedkv.h.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <vector>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+// Read on every call so that a process can switch validation on and off.
+bool debug_validate_enabled() {
+  const char *v = getenv("PKV_DEBUG_VALIDATE");
+  return v != nullptr && v[0] != '\0' && strcmp(v, "0") != 0;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pkv_status copy_to_host(std::vector<int32_t> &dst, const int32_t *src, size_t n, hipStream_t stream) {
+  dst.resize(n);
+  if (n == 0) return PKV_OK;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return PKV_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_cu_count[kMaxDevices];
+
+}  // namespace
+
+extern "C" const char *pkv_status_string(pkv_status status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "invalid size or scale argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported geometry (needs block_size 16, head_dim 64, 4 query heads per KV head)";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small for the context split";
+    case PKV_ERR_VALIDATION: return "debug validation rejected the block table, positions or context lengths";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_ALIGNMENT: return "a device buffer is not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+extern "C" int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+extern "C" int32_t pkv_device_cu_count(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int32_t cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return -1;
+  if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+extern "C" int32_t pkv_plan_partition_pages(int32_t batch, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                                            int32_t num_cus) {
+  if (batch < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_cus <= 0) return -1;
+  const int64_t pairs = (int64_t)batch * num_kv_heads;
+  const int64_t target = 4LL * num_cus;  // ~4 resident 4-wavefront workgroups per CU
+  if (pairs == 0 || 2 * pairs >= target) return max_blocks_per_seq;
+  int64_t pages = ((int64_t)max_blocks_per_seq * pairs + target - 1) / target;
+  pages = ((pages + 3) / 4) * 4;  // one page per wavefront at least, equal shares
+  if (pages < 4) pages = 4;
+  return pages >= max_blocks_per_seq ? max_blocks_per_seq : (int32_t)pages;
+}
+
+extern "C" size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                             int32_t partition_pages) {
+  if (batch < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_pages <= 0) return 0;
+  const int64_t parts = ((int64_t)max_blocks_per_seq + partition_pages - 1) / partition_pages;
+  if (parts <= 1) return 0;
+  const int64_t slots = (int64_t)batch * num_q_heads * parts;
+  return (size_t)slots * (pkv::kHeadDim + 2) * sizeof(float);
+}
+
+extern "C" pkv_status pkv_kv_append(const pkv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *positions, const void *k_new, const void *v_new, int32_t batch,
+                                    void *stream) {
+  if (!pool) return PKV_ERR_NULL;
+  if (batch < 0 || max_blocks_per_seq <= 0 || pool->num_pages <= 0 || pool->num_kv_heads <= 0) return PKV_ERR_SHAPE;
+  if (pool->head_dim != pkv::kHeadDim || pool->block_size != pkv::kBlock) return PKV_ERR_UNSUPPORTED;
+  if (batch == 0) return PKV_OK;
+  if (!pool->k_pool || !pool->v_pool || !block_tables || !positions || !k_new || !v_new) return PKV_ERR_NULL;
+  if (!aligned16(pool->k_pool) || !aligned16(pool->v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return PKV_ERR_ALIGNMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (debug_validate_enabled()) {
+    std::vector<int32_t> bt, pos;
+    pkv_status st = copy_to_host(bt, block_tables, (size_t)batch * max_blocks_per_seq, s);
+    if (st == PKV_OK) st = copy_to_host(pos, positions, (size_t)batch, s);
+    if (st != PKV_OK) return st;
+    st = pkv_validate_append_host(bt.data(), max_blocks_per_seq, pos.data(), batch, pool->num_pages, nullptr);
+    if (st != PKV_OK) return st;
+  }
+
+  pkv::AppendParams p;
+  p.k_pool = static_cast<uint16_t *>(pool->k_pool);
+  p.v_pool = static_cast<uint16_t *>(pool->v_pool);
+  p.block_tables = block_tables;
+  p.positions = positions;
+  p.k_new = static_cast<const uint16_t *>(k_new);
+  p.v_new = static_cast<const uint16_t *>(v_new);
+  p.num_pages = pool->num_pages;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.max_blocks = max_blocks_per_seq;
+  p.batch = batch;
+  return pkv::launch_kv_append(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" pkv_status pkv_paged_decode_attention(const void *q, const void *k_pool, const void *v_pool,
+                                                 int32_t num_pages, const int32_t *block_tables,
+                                                 int32_t max_blocks_per_seq, const int32_t *context_lens, void *out,
+                                                 pkv_out_dtype out_dtype, int32_t batch, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                 float scale, int32_t partition_pages, void *workspace,
+                                                 size_t workspace_bytes, void *stream) {
+  if (batch < 0 || num_pages <= 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0)
+    return PKV_ERR_SHAPE;
+  if (!(scale > 0.0f) || !isfinite(scale)) return PKV_ERR_SHAPE;
+  if (out_dtype != PKV_OUT_BF16 && out_dtype != PKV_OUT_F32) return PKV_ERR_SHAPE;
+  if (head_dim != pkv::kHeadDim || block_size != pkv::kBlock || num_q_heads != pkv::kGroup * num_kv_heads)
+    return PKV_ERR_UNSUPPORTED;
+  if (batch == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PKV_ERR_ALIGNMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  int32_t part_pages = partition_pages;
+  if (part_pages <= 0) {
+    const int32_t cus = pkv_device_cu_count();
+    if (cus <= 0) return PKV_ERR_HIP;
+    part_pages = pkv_plan_partition_pages(batch, num_kv_heads, max_blocks_per_seq, cus);
+  }
+  if (part_pages > max_blocks_per_seq) part_pages = max_blocks_per_seq;
+  const int32_t num_parts = (max_blocks_per_seq + part_pages - 1) / part_pages;
+  if (num_parts > 1) {
+    const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, max_blocks_per_seq, part_pages);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGNMENT;
+  }
+
+  if (debug_validate_enabled()) {
+    std::vector<int32_t> bt, lens;
+    pkv_status st = copy_to_host(bt, block_tables, (size_t)batch * max_blocks_per_seq, s);
+    if (st == PKV_OK) st = copy_to_host(lens, context_lens, (size_t)batch, s);
+    if (st != PKV_OK) return st;
+    st = pkv_validate_decode_host(bt.data(), max_blocks_per_seq, lens.data(), batch, num_pages, nullptr);
+    if (st != PKV_OK) return st;
+  }
+
+  pkv::DecodeParams p;
+  p.q = static_cast<const uint16_t *>(q);
+  p.k_pool = static_cast<const uint16_t *>(k_pool);
+  p.v_pool = static_cast<const uint16_t *>(v_pool);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.part_o = nullptr;
+  p.part_ml = nullptr;
+  if (num_parts > 1) {
+    const int64_t slots = (int64_t)batch * num_q_heads * num_parts;
+    p.part_o = static_cast<float *>(workspace);
+    p.part_ml = p.part_o + slots * pkv::kHeadDim;
+  }
+  p.num_pages = num_pages;
+  p.max_blocks = max_blocks_per_seq;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.part_pages = part_pages;
+  p.num_parts = num_parts;
+  p.score_log2 = scale * 1.4426950408889634f;
+  return pkv::launch_paged_decode(p, out_dtype == PKV_OUT_BF16, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}

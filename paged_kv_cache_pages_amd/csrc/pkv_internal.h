@@ -1,0 +1,50 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernels of libpagedkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Compiled geometry: 16-token pages, head_dim 64, four query heads per KV head.
+constexpr int kBlock = 16;
+constexpr int kHeadDim = 64;
+constexpr int kGroup = 4;
+
+struct AppendParams {
+  uint16_t *k_pool;
+  uint16_t *v_pool;
+  const int32_t *block_tables;
+  const int32_t *positions;
+  const uint16_t *k_new;
+  const uint16_t *v_new;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t batch;
+};
+
+struct DecodeParams {
+  const uint16_t *q;
+  const uint16_t *k_pool;
+  const uint16_t *v_pool;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  void *out;
+  float *part_o;   // [batch][num_q_heads][num_parts][kHeadDim], un-normalised partial sums
+  float *part_ml;  // [batch][num_q_heads][num_parts][2]: (running max in log2 units, denominator)
+  int32_t num_pages;
+  int32_t max_blocks;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t part_pages;  // pages per partition
+  int32_t num_parts;   // ceil(max_blocks / part_pages)
+  float score_log2;    // scale * log2(e): scores are kept in log2 units so exp2 does the softmax
+};
+
+hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
+hipError_t launch_paged_decode(const DecodeParams &p, bool out_bf16, hipStream_t stream);
+
+}  // namespace pkv

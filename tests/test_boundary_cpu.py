@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and its synchronous
+host checks return the documented status codes before anything reaches the device."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_pages_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+OK, NULL, SHAPE, UNSUP, WS, VALID, HIP, ALIGN = range(8)
+FAKE = 0x10000  # a 16-byte aligned non-null address that the checks below never dereference
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkv.LIB_PATH):
+        pytest.fail("libpagedkv.so is not built (run __graft_entry__.build())")
+    return pkv.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    assert set(names) == set(pkv.SIGNATURES), "binding signatures and header disagree"
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.pkv_abi_version() == 1
+    for code in range(8):
+        assert lib.pkv_status_string(code)
+    assert b"aligned" in lib.pkv_status_string(ALIGN)
+
+
+def test_partition_planning():
+    plan = lambda b, h, t, c: pkv.plan_partition_pages(b, h, t, num_cus=c)
+    assert plan(256, 8, 128, 256) == 128  # 2048 (sequence, head) workgroups: no split
+    assert plan(1, 8, 128, 256) == 4  # one long sequence: 32 partitions of 4 pages
+    assert plan(16, 8, 128, 256) == 16
+    assert plan(17, 8, 128, 256) == 20
+    assert plan(64, 8, 128, 256) == 128
+    for b in range(0, 300, 7):
+        p = plan(b, 8, 128, 256)
+        assert 4 <= p <= 128 and (p == 128 or p % 4 == 0)
+    assert pkv.library().pkv_plan_partition_pages(-1, 8, 128, 256) == -1
+
+
+def test_workspace_bytes():
+    assert pkv.decode_workspace_bytes(4, 32, 128, 128) == 0
+    assert pkv.decode_workspace_bytes(4, 32, 128, 200) == 0
+    assert pkv.decode_workspace_bytes(1, 32, 128, 4) == 1 * 32 * 32 * 66 * 4
+    assert pkv.decode_workspace_bytes(3, 32, 128, 20) == 3 * 32 * 7 * 66 * 4
+
+
+def _append(lib, pool, bt=FAKE, maxb=128, pos=FAKE, k=FAKE, v=FAKE, batch=1):
+    return lib.pkv_kv_append(pool, bt, maxb, pos, k, v, batch, None)
+
+
+def test_append_host_checks(lib):
+    good = pkv.Pool(FAKE, FAKE, 8, 8, 64, 16)
+    assert _append(lib, None) == NULL
+    assert _append(lib, ctypes.byref(pkv.Pool(FAKE, FAKE, 8, 8, 128, 16))) == UNSUP
+    assert _append(lib, ctypes.byref(pkv.Pool(FAKE, FAKE, 8, 8, 64, 32))) == UNSUP
+    assert _append(lib, ctypes.byref(pkv.Pool(FAKE, FAKE, 0, 8, 64, 16))) == SHAPE
+    assert _append(lib, ctypes.byref(good), batch=-1) == SHAPE
+    assert _append(lib, ctypes.byref(good), maxb=0) == SHAPE
+    assert _append(lib, ctypes.byref(good), batch=0) == OK  # no-op, nothing enqueued
+    assert _append(lib, ctypes.byref(good), bt=None) == NULL
+    assert _append(lib, ctypes.byref(good), k=None) == NULL
+    assert _append(lib, ctypes.byref(good), k=FAKE + 2) == ALIGN
+    assert _append(lib, ctypes.byref(pkv.Pool(FAKE + 8, FAKE, 8, 8, 64, 16))) == ALIGN
+
+
+def _decode(lib, q=FAKE, kp=FAKE, vp=FAKE, pages=8, bt=FAKE, maxb=128, lens=FAKE, out=FAKE, odt=0, batch=1, hq=32,
+            hkv=8, d=64, bs=16, scale=0.125, pp=128, ws=None, wsb=0):
+    return lib.pkv_paged_decode_attention(q, kp, vp, pages, bt, maxb, lens, out, odt, batch, hq, hkv, d, bs, scale, pp,
+                                          ws, wsb, None)
+
+
+def test_decode_host_checks(lib):
+    assert _decode(lib, batch=-1) == SHAPE
+    assert _decode(lib, pages=0) == SHAPE
+    assert _decode(lib, scale=0.0) == SHAPE
+    assert _decode(lib, scale=float("nan")) == SHAPE
+    assert _decode(lib, scale=float("inf")) == SHAPE
+    assert _decode(lib, odt=7) == SHAPE
+    assert _decode(lib, d=128) == UNSUP
+    assert _decode(lib, bs=32) == UNSUP
+    assert _decode(lib, hq=16) == UNSUP  # group of 2
+    assert _decode(lib, batch=0) == OK
+    assert _decode(lib, q=None) == NULL
+    assert _decode(lib, lens=None) == NULL
+    assert _decode(lib, out=FAKE + 4) == ALIGN
+    # an explicit split needs a workspace of the documented size
+    need = pkv.decode_workspace_bytes(1, 32, 128, 4)
+    assert _decode(lib, pp=4) == WS
+    assert _decode(lib, pp=4, ws=FAKE, wsb=need - 1) == WS
+    assert _decode(lib, pp=4, ws=FAKE + 8, wsb=need) == ALIGN
+
+
+def test_host_validators():
+    bt = np.full((3, 4), -1, dtype=np.int32)
+    bt[0, :2] = [5, 6]
+    bt[1, :1] = [2]
+    bt[2, :4] = [0, 1, 3, 4]
+    assert pkv.validate_decode_host(bt, [20, 16, 64], 8) == (OK, -1)
+    assert pkv.validate_decode_host(bt, [20, 17, 64], 8) == (VALID, 1)  # needs block 1 of row 1
+    assert pkv.validate_decode_host(bt, [20, 16, 65], 8) == (VALID, 2)  # beyond the table
+    assert pkv.validate_decode_host(bt, [-1, 16, 64], 8) == (VALID, 0)
+    assert pkv.validate_decode_host(bt, [0, 0, 0], 8) == (OK, -1)
+    assert pkv.validate_decode_host(bt, [20, 16, 64], 6) == (VALID, 0)  # row 0 holds page 6 of a 6-page pool
+    assert pkv.validate_append_host(bt, [19, 15, 63], 8) == (OK, -1)
+    assert pkv.validate_append_host(bt, [19, 16, 63], 8) == (VALID, 1)  # block 1 unassigned
+    assert pkv.validate_append_host(bt, [19, 15, 64], 8) == (VALID, 2)  # position past the table
+    bt2 = bt.copy()
+    bt2[1, 0] = 6
+    assert pkv.validate_append_host(bt2, [19, 3, 63], 8) == (VALID, 1)  # same (page 6, slot 3) twice
+    assert pkv.validate_append_host(bt2, [19, 4, 63], 8) == (OK, -1)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from paged_kv_cache_pages_amd import _binding
+
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "libpagedkv.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        _binding.library()

@@ -1,0 +1,325 @@
+"""GPU parity: the HIP path through the C ABI against the FP64 oracle on the same seeded inputs.
+
+kv_append must be bit-exact over the whole pool.  Attention (FP32 output) must satisfy
+|gpu - oracle| <= 2e-3 + 1e-2 |oracle| elementwise, and the BF16 output must be the
+round-to-nearest-even of the FP32 output bit for bit.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import assert_close, bf16_to_bits, layer_tensors, to_gpu_bf16, to_gpu_i32, upload
+from workloads import make_config, make_custom
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = ["tiny", "long", "mixed", "model16", "bw256"]
+NAN_BITS = np.uint16(0x7FC0)
+
+_cache = {}
+
+
+def config(name):
+    if name not in _cache:
+        _cache.clear()  # keep at most one large workload alive
+        _cache[name] = make_config(name)
+    return _cache[name]
+
+
+def sampled_rows(w):
+    """All sequences up to 256 (the oracle takes ~20 ms per 2048-token sequence); beyond that 24
+    spread-out rows."""
+    if w.batch <= 256:
+        return None
+    rng = np.random.default_rng(1234)
+    rows = set([0, w.batch - 1]) | set(rng.choice(w.batch, size=22, replace=False).tolist())
+    return sorted(rows)
+
+
+def attend(gpu, q, kp, vp, bt, lens, **kw):
+    import torch
+
+    kw.setdefault("out_dtype", torch.float32)
+    return gpu.paged_decode_attention(q, kp, vp, bt, lens, **kw)
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_append_bit_exact(gpu, name):
+    import torch
+
+    w = config(name)
+    print(f"[append] config={name} B={w.batch} layers={w.layers} pages={w.num_pages}", flush=True)
+    kp, vp = to_gpu_bf16(w.k_pool), to_gpu_bf16(w.v_pool)
+    pos = to_gpu_i32(w.positions)
+    ref_k, ref_v = w.k_pool, w.v_pool
+    for layer in range(w.layers):
+        t = layer_tensors(w, layer)
+        gpu.kv_append(kp, vp, t["block_tables"], pos, t["k_new"], t["v_new"])
+        ref_k, ref_v = oracle.kv_append(ref_k, ref_v, w.block_tables[layer], w.positions, w.k_new[layer], w.v_new[layer])
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_bits(kp), ref_k)
+    assert np.array_equal(bf16_to_bits(vp), ref_v)
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_attention_parity(gpu, name):
+    """Append, then attend over L = pos + 1 (the new token included), every layer."""
+    import torch
+
+    w = config(name)
+    rows = sampled_rows(w)
+    print(f"[attention] config={name} B={w.batch} layers={w.layers} rows={rows}", flush=True)
+    kp, vp = to_gpu_bf16(w.k_pool), to_gpu_bf16(w.v_pool)
+    pos, lens = to_gpu_i32(w.positions), to_gpu_i32(w.context_lens)
+    ref_k, ref_v = w.k_pool, w.v_pool
+    for layer in range(w.layers):
+        t = layer_tensors(w, layer)
+        gpu.kv_append(kp, vp, t["block_tables"], pos, t["k_new"], t["v_new"])
+        out32 = attend(gpu, t["q"], kp, vp, t["block_tables"], lens)
+        out16 = attend(gpu, t["q"], kp, vp, t["block_tables"], lens, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        ref_k, ref_v = oracle.kv_append(ref_k, ref_v, w.block_tables[layer], w.positions, w.k_new[layer], w.v_new[layer])
+        ref = oracle.paged_decode_attention(w.q[layer], ref_k, ref_v, w.block_tables[layer], w.context_lens, 0.125,
+                                            sequences=rows)
+        got = out32.cpu().numpy()
+        sel = slice(None) if rows is None else rows
+        abs_err, rel_err = assert_close(got[sel], ref[sel], f"{name} layer {layer}")
+        print(f"  layer {layer}: max abs {abs_err:.3e}, max rel {rel_err:.3e}", flush=True)
+        assert np.array_equal(bf16_to_bits(out16), oracle.bf16_round_nearest_even(got))
+
+
+RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000, 2047, 2048]
+
+
+@pytest.mark.parametrize("partition_pages", [0, 4, 8, 12, 128])
+def test_ragged_lengths_and_splits(gpu, partition_pages):
+    w = make_custom(seed=21, lengths=RAGGED)
+    d = upload(w)
+    print(f"[ragged] partition_pages={partition_pages}", flush=True)
+    out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                 partition_pages=partition_pages)
+    ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens)
+    assert_close(out.cpu().numpy(), ref, f"ragged pp={partition_pages}")
+
+
+def test_split_matches_unsplit(gpu):
+    w = make_custom(seed=22, lengths=[3, 100, 700, 2048, 1500, 64])
+    d = upload(w)
+    base = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"], partition_pages=128)
+    for pp in (4, 16, 20, 64):
+        other = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"], partition_pages=pp)
+        diff = (base - other).abs().max().item()
+        assert diff <= 1e-5, f"partition_pages={pp}: {diff}"
+
+
+def test_single_token_returns_v_row_exactly(gpu):
+    """L = 1: the only probability is exactly 1, so the FP32 output is the appended V row."""
+    import torch
+
+    w = make_custom(seed=23, lengths=[1, 1, 1])
+    d = upload(w)
+    gpu.kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["positions"], d["k_new"], d["v_new"])
+    out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"])
+    torch.cuda.synchronize()
+    expect = oracle.bf16_bits_to_f64(w.v_new[0]).astype(np.float32)  # [B][Hkv][D]
+    got = out.cpu().numpy()
+    for h in range(32):
+        assert np.array_equal(got[:, h], expect[:, h // 4]), f"head {h}"
+
+
+def test_equal_scores_give_mean_of_values(gpu):
+    """q = 0: every probability is equal and the output is the plain mean of the V rows."""
+    w = make_custom(seed=24, lengths=[5, 77, 300])
+    w.q[:] = 0
+    d = upload(w)
+    out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"]).cpu().numpy()
+    for b, L in enumerate(w.context_lens):
+        vals = oracle.bf16_bits_to_f64(oracle.gather_context(w.v_pool, w.block_tables[0, b], int(L)))
+        mean = vals.mean(axis=0)  # [Hkv][D]
+        for h in range(32):
+            assert np.max(np.abs(out[b, h] - mean[h // 4])) <= 1e-5
+
+
+def test_page_permutation_bit_identical(gpu):
+    """Renaming physical pages (moving their contents along) leaves the output bit-identical."""
+    w = make_custom(seed=25, lengths=[9, 160, 600, 33], num_pages=64)
+    d = upload(w)
+    base = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"])
+    perm = np.random.default_rng(3).permutation(w.num_pages)
+    k2 = np.empty_like(w.k_pool)
+    v2 = np.empty_like(w.v_pool)
+    k2[perm] = w.k_pool
+    v2[perm] = w.v_pool
+    bt2 = np.where(w.block_tables[0] >= 0, perm[np.maximum(w.block_tables[0], 0)], -1)
+    moved = attend(gpu, d["q"], to_gpu_bf16(k2), to_gpu_bf16(v2), to_gpu_i32(bt2), d["context_lens"])
+    assert np.array_equal(base.cpu().numpy(), moved.cpu().numpy())
+
+
+def poison_outside_context(w, layer=0):
+    keep = np.zeros((w.num_pages, 16), dtype=bool)
+    for b in range(w.batch):
+        for t in range(int(w.context_lens[b])):
+            keep[w.block_tables[layer, b, t // 16], t % 16] = True
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    kp.transpose(0, 2, 1, 3)[~keep] = NAN_BITS
+    vp.transpose(0, 2, 1, 3)[~keep] = NAN_BITS
+    return kp, vp
+
+
+@pytest.mark.parametrize("partition_pages", [0, 128])
+def test_nan_outside_context_changes_nothing(gpu, partition_pages):
+    w = make_custom(seed=26, lengths=[1, 7, 16, 17, 250, 1023], num_pages=120)
+    d = upload(w)
+    clean = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                   partition_pages=partition_pages).cpu().numpy()
+    kp, vp = poison_outside_context(w)
+    dirty = attend(gpu, d["q"], to_gpu_bf16(kp), to_gpu_bf16(vp), d["block_tables"], d["context_lens"],
+                   partition_pages=partition_pages).cpu().numpy()
+    assert np.all(np.isfinite(dirty))
+    assert np.array_equal(clean, dirty)
+
+
+def test_append_into_nan_pool_touches_only_targets(gpu):
+    import torch
+
+    w = make_custom(seed=27, lengths=[1, 16, 17, 40, 33, 2048], num_pages=200)
+    kp = np.full_like(w.k_pool, NAN_BITS)
+    vp = np.full_like(w.v_pool, NAN_BITS)
+    dk, dv = to_gpu_bf16(kp), to_gpu_bf16(vp)
+    gpu.kv_append(dk, dv, to_gpu_i32(w.block_tables[0]), to_gpu_i32(w.positions), to_gpu_bf16(w.k_new[0]),
+                  to_gpu_bf16(w.v_new[0]))
+    torch.cuda.synchronize()
+    rk, rv = oracle.kv_append(kp, vp, w.block_tables[0], w.positions, w.k_new[0], w.v_new[0])
+    assert np.array_equal(bf16_to_bits(dk), rk)
+    assert np.array_equal(bf16_to_bits(dv), rv)
+
+
+def test_zero_length_rows_are_zero(gpu):
+    w = make_custom(seed=28, lengths=[0, 5, 0, 40])
+    d = upload(w)
+    for pp in (0, 4, 128):
+        out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                     partition_pages=pp).cpu().numpy()
+        assert np.all(out[0] == 0) and np.all(out[2] == 0)
+        ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens)
+        assert_close(out, ref, f"zero-length pp={pp}")
+
+
+@pytest.mark.parametrize("partition_pages", [4, 128])
+@pytest.mark.parametrize("bad_entry", [-1, "num_pages", 1 << 30])
+def test_invalid_page_id_zeroes_only_that_sequence(gpu, partition_pages, bad_entry):
+    """An out-of-range table entry inside a context is never dereferenced: that sequence's output
+    is zero and the other sequences are unchanged."""
+    w = make_custom(seed=29, lengths=[70, 300, 45])
+    d = upload(w)
+    good = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                  partition_pages=partition_pages).cpu().numpy()
+    bt = w.block_tables[0].copy()
+    bt[1, 13] = w.num_pages if bad_entry == "num_pages" else bad_entry
+    out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], to_gpu_i32(bt), d["context_lens"],
+                 partition_pages=partition_pages).cpu().numpy()
+    assert np.all(out[1] == 0)
+    assert np.array_equal(out[0], good[0]) and np.array_equal(out[2], good[2])
+
+
+def test_invalid_context_length_zeroes_sequence(gpu):
+    w = make_custom(seed=30, lengths=[20, 50])
+    d = upload(w)
+    for bad_len in (-3, 128 * 16 + 1):
+        lens = w.context_lens.copy()
+        lens[0] = bad_len
+        for pp in (4, 128):
+            out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], to_gpu_i32(lens),
+                         partition_pages=pp).cpu().numpy()
+            assert np.all(out[0] == 0)
+            assert np.all(np.isfinite(out[1])) and np.any(out[1] != 0)
+
+
+def test_append_skips_out_of_range_rows(gpu):
+    import torch
+
+    w = make_custom(seed=31, lengths=[10, 20, 30])
+    pos = w.positions.copy()
+    pos[0] = -1
+    pos[2] = 128 * 16
+    bt = w.block_tables[0].copy()
+    bt[1, 1] = -1  # position 19 -> block 1 unassigned
+    d = upload(w)
+    gpu.kv_append(d["k_pool"], d["v_pool"], to_gpu_i32(bt), to_gpu_i32(pos), d["k_new"], d["v_new"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_bits(d["k_pool"]), w.k_pool)
+    assert np.array_equal(bf16_to_bits(d["v_pool"]), w.v_pool)
+
+
+def test_debug_validation_rejects_bad_data(gpu):
+    import torch
+
+    w = make_custom(seed=32, lengths=[10, 20])
+    d = upload(w)
+    bt = w.block_tables[0].copy()
+    bt[1, 0] = -1
+    os.environ["PKV_DEBUG_VALIDATE"] = "1"
+    try:
+        gpu.kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["positions"], d["k_new"], d["v_new"])
+        attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"])
+        with pytest.raises(gpu.PagedKVError, match="PKV_ERR_VALIDATION"):
+            attend(gpu, d["q"], d["k_pool"], d["v_pool"], to_gpu_i32(bt), d["context_lens"])
+        same = w.positions.copy()
+        same[1] = same[0]
+        bt2 = w.block_tables[0].copy()
+        bt2[1, 0] = bt2[0, 0]
+        with pytest.raises(gpu.PagedKVError, match="PKV_ERR_VALIDATION"):
+            gpu.kv_append(d["k_pool"], d["v_pool"], to_gpu_i32(bt2), to_gpu_i32(same), d["k_new"], d["v_new"])
+    finally:
+        del os.environ["PKV_DEBUG_VALIDATE"]
+    torch.cuda.synchronize()
+
+
+def test_long_table_reloads_page_ids(gpu):
+    """A 300-entry table with no split: one wavefront walks more than 64 pages."""
+    w = make_custom(seed=33, lengths=[4500, 1100], max_blocks=300)
+    d = upload(w)
+    out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"], partition_pages=300)
+    ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens)
+    assert_close(out.cpu().numpy(), ref, "long table")
+
+
+def test_other_kv_head_counts(gpu):
+    """The group of four query heads per KV head is fixed; the number of KV heads is not."""
+    for hkv in (1, 2, 5):
+        w = make_custom(seed=34 + hkv, lengths=[33, 400, 1], num_kv_heads=hkv)
+        d = upload(w)
+        gpu.kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["positions"], d["k_new"], d["v_new"])
+        out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"])
+        rk, rv = oracle.kv_append(w.k_pool, w.v_pool, w.block_tables[0], w.positions, w.k_new[0], w.v_new[0])
+        ref = oracle.paged_decode_attention(w.q[0], rk, rv, w.block_tables[0], w.context_lens)
+        assert_close(out.cpu().numpy(), ref, f"hkv={hkv}")
+
+
+def test_runs_on_the_callers_stream(gpu):
+    import torch
+
+    w = make_custom(seed=40, lengths=[500, 37])
+    d = upload(w)
+    ref = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"])
+    s.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_batch_zero_is_a_no_op(gpu):
+    import torch
+
+    e = torch.empty
+    kp = e((4, 8, 16, 64), dtype=torch.bfloat16, device="cuda")
+    gpu.kv_append(kp, kp.clone(), e((0, 8), dtype=torch.int32, device="cuda"), e((0,), dtype=torch.int32, device="cuda"),
+                  e((0, 8, 64), dtype=torch.bfloat16, device="cuda"), e((0, 8, 64), dtype=torch.bfloat16, device="cuda"))
+    out = gpu.paged_decode_attention(e((0, 32, 64), dtype=torch.bfloat16, device="cuda"), kp, kp,
+                                     e((0, 8), dtype=torch.int32, device="cuda"), e((0,), dtype=torch.int32, device="cuda"))
+    assert out.shape == (0, 32, 64)
