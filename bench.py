@@ -1,0 +1,301 @@
+"""Decode-step benchmark: kv_append + paged decode attention on one MI355X.
+
+One step is the whole hot path over one synthetic batch: every layer's kv_append (each sequence's
+new K/V row into its page), then every layer's paged decode attention (plus the partition merge
+when the context is split).  Inputs are generated on the host with the seeded generators and are
+resident in HBM before timing starts.  The default workload is 256 sequences at context 2048
+(32768 pages, 1 GiB of BF16 K+V).
+
+Prints ONE JSON line.  ``value`` is algorithmic GB/s of the whole step (bytes / wall time per
+step); ``roofline`` reports the attention kernel against the 8 TB/s HBM peak using HIP events
+recorded around each launch on the stream the kernel runs on; ``cpu_baseline`` times the FP64 CPU
+oracle on the host cores.  The pages report no throughput or hardware numbers for this kernel,
+so ``vs_baseline`` is null.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged decode attention GB/s and % of HBM peak; seq-tokens attended/sec"
+ATTN_SOURCE = os.path.join(ROOT, "paged_kv_cache_pages_amd", "csrc", "paged_attention.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_bw256_traffic.md")
+
+WORKLOAD_TEXT = {
+    "tiny": "1 sequence, context 37 (3 pages, last partial), 8-page pool",
+    "long": "1 sequence, context 2048 (128 pages), 512-page pool, split context + merge",
+    "mixed": "16 sequences, context uniform in [1,2048], 2048-page pool",
+    "model16": "16 layers, 128 MiB pool (4096 pages), FIFO-admitted batch, geometric contexts (mean 256)",
+    "bw256": "256 sequences x context 2048, 32768 pages (1 GiB BF16 K+V), random page order",
+}
+
+
+# ---------------------------------------------------------------------------------------------
+# byte accounting (algorithmic bytes: what the step must move at least once)
+# ---------------------------------------------------------------------------------------------
+
+def attention_bytes(w) -> int:
+    """Q + every referenced K/V page (whole pages) + referenced table entries + BF16 output."""
+    hq, d, hkv = w.num_q_heads, w.head_dim, w.num_kv_heads
+    pages = int(np.sum((w.context_lens.astype(np.int64) + 15) // 16))
+    page_bytes = 2 * hkv * 16 * d * 2  # K and V of one page, all KV heads
+    per_layer = w.batch * (hq * d * 2) * 2 + pages * page_bytes + pages * 4
+    return per_layer * w.layers
+
+
+def append_bytes(w) -> int:
+    """k_new + v_new read, the same rows written, one position and one table entry per row."""
+    row = w.num_kv_heads * w.head_dim * 2
+    return w.layers * w.batch * (2 * row + 2 * row + 4 + 4)
+
+
+def seq_tokens(w) -> int:
+    return int(w.context_lens.sum()) * w.layers
+
+
+# ---------------------------------------------------------------------------------------------
+# HBM traffic measured with rocprofv3 counters (taken offline, recorded under profiles/)
+# ---------------------------------------------------------------------------------------------
+
+def kernel_source_digest() -> str:
+    """Hash of the attention kernel's code with comments and whitespace removed, so the recorded
+    counters stay valid across comment-only edits and lapse on any code change."""
+    with open(ATTN_SOURCE) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
+def recorded_traffic():
+    """Traffic per launch from the committed counter summary, or None when the kernel source has
+    changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_val) or m_src.group(1) != kernel_source_digest():
+        return None
+    return float(m_val.group(1))
+
+
+# ---------------------------------------------------------------------------------------------
+# CPU baseline: the FP64 oracle as it stands, on the host
+# ---------------------------------------------------------------------------------------------
+
+def cpu_baseline(w, max_seconds: float):
+    """Time the oracle's append + attention over a prefix of the batch (all layers).
+
+    Sequences are processed in order until ``max_seconds`` of work has been done or the batch
+    ends; the rate is reported in the same GB/s units as ``value`` (algorithmic bytes of the
+    sequences processed / seconds).  BLAS is pinned to one thread, so ``cores`` is 1.
+    """
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    bytes_per_seq = (attention_bytes(w) + append_bytes(w)) / w.batch
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for layer in range(w.layers):
+            k, v = oracle.kv_append(w.k_pool, w.v_pool, w.block_tables[layer], w.positions, w.k_new[layer],
+                                    w.v_new[layer])
+        chunk = 8
+        b = 0
+        while b < w.batch and (time.perf_counter() - t0) < max_seconds:
+            rows = list(range(b, min(w.batch, b + chunk)))
+            for layer in range(w.layers):
+                oracle.paged_decode_attention(w.q[layer], k, v, w.block_tables[layer], w.context_lens, 0.125,
+                                              sequences=rows)
+            b += len(rows)
+            done = b
+        secs = time.perf_counter() - t0
+    gbps = bytes_per_seq * done / secs / 1e9
+    return {
+        "value": round(gbps, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {w.batch} sequences x {w.layers} layer(s) of the same workload (FP64 numpy, "
+                  f"append of the whole pool + attention), {secs:.2f} s",
+        "seconds": round(secs, 3),
+        "seq_tokens_per_s": round(float(w.context_lens[:done].sum()) * w.layers / secs, 1),
+    }
+
+
+# ---------------------------------------------------------------------------------------------
+# GPU run
+# ---------------------------------------------------------------------------------------------
+
+def run(args):
+    import torch
+
+    import paged_kv_cache_pages_amd as pkv
+    from workloads import make_config
+
+    pkv.require_library()
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    w = make_config(args.config)
+    gen_s = time.perf_counter() - t_gen
+    print(f"[bench] workload {args.config}: B={w.batch} layers={w.layers} pages={w.num_pages} "
+          f"(generated in {gen_s:.1f} s)", file=sys.stderr, flush=True)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    def dev_i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    kp, vp = dev_bf16(w.k_pool), dev_bf16(w.v_pool)
+    pos, lens = dev_i32(w.positions), dev_i32(w.context_lens)
+    layers = []
+    for layer in range(w.layers):
+        layers.append({
+            "bt": dev_i32(w.block_tables[layer]),
+            "q": dev_bf16(w.q[layer]),
+            "k_new": dev_bf16(w.k_new[layer]),
+            "v_new": dev_bf16(w.v_new[layer]),
+            "out": torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda"),
+        })
+    pp = args.partition_pages if args.partition_pages > 0 else pkv.plan_partition_pages(
+        w.batch, w.num_kv_heads, w.max_blocks)
+    ws_bytes = pkv.decode_workspace_bytes(w.batch, w.num_q_heads, w.max_blocks, pp)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def append_all():
+        for t in layers:
+            pkv.kv_append(kp, vp, t["bt"], pos, t["k_new"], t["v_new"])
+
+    def attend_all():
+        for t in layers:
+            pkv.paged_decode_attention(t["q"], kp, vp, t["bt"], lens, t["out"], partition_pages=pp,
+                                       workspace=workspace)
+
+    for _ in range(args.warmup):
+        append_all()
+        attend_all()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        append_all()
+        ev[i][1].record()
+        attend_all()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    append_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+
+    # plain device-to-device copy of 1 GiB (2 GiB moved) as an achievable-bandwidth reference
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    ms_per_step = wall_s * 1e3 / K
+    a_bytes, p_bytes = attention_bytes(w), append_bytes(w)
+    step_bytes = a_bytes + p_bytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # one "launch" of the attention kernel = one layer's decode attention
+    attn_launch_ms = float(np.mean(attn_ms)) / w.layers
+    attn_gbps = (a_bytes / w.layers) / (attn_launch_ms * 1e-3) / 1e9
+    traffic = recorded_traffic() if pp >= w.max_blocks and args.config == "bw256" else None
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "compute": "bf16 inputs, f32 accumulate and softmax",
+        "data": "synthetic (seeded N(0,1) BF16; no dataset)",
+        "config": {
+            "workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}",
+            "batch": w.batch,
+            "layers": w.layers,
+            "context_tokens": seq_tokens(w),
+            "q_heads": w.num_q_heads,
+            "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": 16,
+            "pool_pages": w.num_pages,
+            "partition_pages": pp,
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "seq_tokens_per_s": round(seq_tokens(w) / (ms_per_step * 1e-3), 1),
+        "bytes_per_step": step_bytes,
+        "attention_us_per_launch": round(attn_launch_ms * 1e3, 3),
+        "append_us_per_step": round(float(np.mean(append_ms)) * 1e3, 3),
+        "copy_d2d_gbps": round(copy_gbps, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(attn_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "paged_decode_kernel" + ("" if pp >= w.max_blocks else " + merge_partitions_kernel"),
+            "algorithmic_bytes_per_launch": a_bytes // w.layers,
+        },
+        "note": "The reference pages report no throughput or hardware numbers for this kernel; "
+                "figures are this build's measurements on one MI355X.",
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="bw256", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--partition-pages", type=int, default=0, help="<= 0: library plan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="bound on the CPU oracle timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this path has no "
+              "multi-GPU mode).", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

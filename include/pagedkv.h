@@ -32,9 +32,9 @@
  *
  * Supported geometry (anything else returns PKV_ERR_UNSUPPORTED): block_size 16, head_dim 64,
  * num_q_heads == 4 * num_kv_heads.  These are the Llama-3.2-1B decode constants of the pages:
- * 16-token pages (jaehun.me, code-series index, part 6 "Splitting the KV cache into 16-token
+ * 16-token pages ("Code-Series on Jaehun's Blog", entry 6 "Splitting the KV cache into 16-token
  * blocks"), 32 query heads over 8 KV heads with consecutive groups of four and head_dim 64
- * (jaehun.me, "The prefill path", section "Per-head attention scores and GQA").
+ * ("The prefill path: flowing the entire prompt at once", section "Per-head attention scores and GQA").
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -89,8 +89,8 @@ int32_t pkv_abi_version(void);
  * K[page][g][slot][:] and v_new[b][g][:] into V[page][g][slot][:], where
  * page = block_tables[b * max_blocks_per_seq + positions[b] / 16] and slot = positions[b] % 16.
  * The pages describe this step as decode appending one new token at its absolute (RoPE)
- * position into the shared BF16 page pool (news.t0.vc/TXJZ, "What works so far"), with the
- * page found through the per-sequence block table (jaehun.me, "The prefill path", section
+ * position into the shared BF16 page pool ("6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference", section "What works so far"), with the
+ * page found through the per-sequence block table ("The prefill path: flowing the entire prompt at once", section
  * "Distributing K/V into paged blocks").  The copy is bit-exact.
  *
  *   pool                host struct; its k_pool / v_pool are device buffers (modified)
@@ -115,9 +115,9 @@ pkv_status pkv_kv_append(const pkv_pool *pool, const int32_t *block_tables, int3
  *   out[b][h][:] = sum_t softmax(s)_t * V[page(t)][g][t % 16][:]
  * with page(t) = block_tables[b * max_blocks_per_seq + t / 16].  The pages' decode attention
  * streams each sequence's cached pages per query head and accumulates weighted values with an
- * FP32 online softmax, gathering no contiguous prefix and storing no scores (news.t0.vc/TXJZ,
+ * FP32 online softmax, gathering no contiguous prefix and storing no scores ("6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference",
  * "What works so far"); the online-softmax merge of partial (max, sum) pairs is the rule of
- * jaehun.me, "The prefill path", section "causalMask and online softmax".  Inputs are BF16,
+ * "The prefill path: flowing the entire prompt at once", section "causalMask and online softmax".  Inputs are BF16,
  * all arithmetic is FP32, the output is FP32 or BF16 (round to nearest even).
  *
  *   q                 device bf16[batch][num_q_heads][head_dim]

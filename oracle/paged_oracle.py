@@ -6,13 +6,13 @@ it; the two meet only through the seeded inputs of the ``workloads`` package.
 
 What it computes, in the plainest reading of the pages:
 
-* **Append** (news.t0.vc/TXJZ, "What works so far": decode appends one new token at its absolute
-  position into a shared BF16 page pool; jaehun.me, "The prefill path", section "Distributing K/V
+* **Append** ("6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference", section "What works so far": decode appends one new token at its absolute
+  position into a shared BF16 page pool; "The prefill path: flowing the entire prompt at once", section "Distributing K/V
   into paged blocks": logical block ``pos // 16`` is looked up in the block table).  The new
   pool equals the old one except that slot ``pos % 16`` of page ``table[pos // 16]`` holds the
   new row, for every KV head.  Pure bit copy, applied in batch order.
-* **Attention** (news.t0.vc/TXJZ, "What works so far": each query head streams its sequence's
-  pages; jaehun.me, "The prefill path", sections "Per-head attention scores and GQA" and
+* **Attention** ("6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference", section "What works so far": each query head streams its sequence's
+  pages; "The prefill path: flowing the entire prompt at once", sections "Per-head attention scores and GQA" and
   "causalMask and online softmax").  The oracle does what the GPU path must avoid: it gathers
   the ``L`` cached tokens into a contiguous prefix, upcasts BF16 exactly to FP64, and runs a
   two-pass softmax per query head, with query head ``h`` reading KV head ``h // 4`` and the
@@ -160,7 +160,7 @@ def merge_states(a, b):
     """Combine two (max, denominator, weighted-sum) softmax states over disjoint token sets.
 
     Both are re-anchored to the larger maximum: m = max(ma, mb), d = da*e^(ma-m) + db*e^(mb-m)
-    (jaehun.me, "The prefill path", section "causalMask and online softmax"); the weighted value
+    ("The prefill path: flowing the entire prompt at once", section "causalMask and online softmax"); the weighted value
     sums are re-anchored the same way.  An empty state has d == 0 and is the identity.
     """
     ma, da, oa = a

@@ -1,8 +1,8 @@
 // kv_append: write each sequence's new K/V row into slot (pos % 16) of page table[pos / 16].
 //
 // The decode step appends one new token per sequence at its absolute position into the shared
-// BF16 page pool (news.t0.vc/TXJZ, "What works so far"); the page is the block-table entry of
-// logical block pos / 16 (jaehun.me, "The prefill path", section "Distributing K/V into paged
+// BF16 page pool ("6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference", section "What works so far"); the page is the block-table entry of
+// logical block pos / 16 ("The prefill path: flowing the entire prompt at once", section "Distributing K/V into paged
 // blocks").  With the [page][kv_head][token][dim] layout every (sequence, KV head) row is one
 // 128-byte run in K and one in V, so the kernel is a scatter of 16-byte vectors: one lane per
 // 16 bytes, 8 lanes per row.  Bits are copied unchanged.

@@ -1,6 +1,6 @@
 // Paged decode attention for gfx950: one workgroup per (sequence, KV head, context partition).
 //
-// What is computed (news.t0.vc/TXJZ, "What works so far"; jaehun.me, "The prefill path",
+// What is computed ("6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference", section "What works so far"; "The prefill path: flowing the entire prompt at once",
 // sections "Per-head attention scores and GQA" and "causalMask and online softmax"): for the
 // four query heads that share KV head g, scores s_t = scale * <q_h, K_t> over the sequence's
 // cached tokens, softmax over t, and the softmax-weighted sum of the V rows.  The pages' decode

@@ -1,5 +1,5 @@
 // C ABI of libpagedkv: synchronous host checks, optional debug validation, kernel dispatch.
-// The two method calls follow the problem statement of news.t0.vc/TXJZ ("What works so far":
+// The two method calls follow the problem statement of "6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference", section "What works so far":
 // decode appends each new token at its absolute position into a shared BF16 page pool through a
 // per-sequence block table, and decode attention streams each sequence's pages with an FP32
 // online softmax).  Argument meaning, layout and error behaviour are documented in pagedkv.h.

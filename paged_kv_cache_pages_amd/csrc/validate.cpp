@@ -1,7 +1,7 @@
 // Host-side validation of block tables, positions and context lengths (plain C++, no GPU).
 //
 // The pages' host code asserts when it meets an impossible page-table state instead of
-// continuing (jaehun.me, "The prefill path", section "Distributing K/V into paged blocks"); the
+// continuing ("The prefill path: flowing the entire prompt at once", section "Distributing K/V into paged blocks"); the
 // library's equivalent is this opt-in check, run before launching when PKV_DEBUG_VALIDATE=1 and
 // callable directly on host arrays.
 #include <stdint.h>

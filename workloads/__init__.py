@@ -8,11 +8,11 @@ the attention or append arithmetic, so both the CPU oracle (``oracle/``) and the
 Geometry follows the Llama-3.2-1B decode shape described in the pages:
 
 * 16-token pages and a per-sequence block table whose entry -1 means "unassigned"
-  (jaehun.me, "The prefill path", section "Distributing K/V into paged blocks").
+  ("The prefill path: flowing the entire prompt at once", section "Distributing K/V into paged blocks").
 * 32 query heads sharing 8 KV heads in consecutive groups of four, head_dim 64
   (same page, section "Per-head attention scores and GQA").
 * A 2048-token context cap and a shared 128 MiB pool whose size does not grow with the
-  request count (news.t0.vc/TXJZ, section "Current scope").
+  request count ("6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference", section "Current scope").
 """
 
 from .configs import (  # noqa: F401

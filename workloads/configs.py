@@ -8,8 +8,8 @@ projections, since the pages measure on no public dataset.
 
 Pages are handed out the way the pages' host code does it: a free list of physical page ids
 is consumed from its back, and a block-table entry of -1 means "not assigned"
-(jaehun.me, "The prefill path", section "Distributing K/V into paged blocks").  A decode step
-appends the token at absolute position ``pos`` (news.t0.vc/TXJZ, "What works so far": decode
+("The prefill path: flowing the entire prompt at once", section "Distributing K/V into paged blocks").  A decode step
+appends the token at absolute position ``pos`` ("6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference", section "What works so far": decode
 appends one new token at its absolute position), so a fresh page is taken only when
 ``pos % 16 == 0``; attention then covers ``L = pos + 1`` tokens.
 
@@ -210,7 +210,7 @@ def make_model16(seed: int = 3, requests: int = 64, pool_pages: int = 4096, laye
     Sixty-four context lengths are drawn geometric with mean 256 and capped at 2048.  Requests
     are admitted in order while the pages they need over all layers (``layers * ceil(L/16)``)
     still fit in the pool; the first request that does not fit stops admission, mirroring the
-    FIFO wait without skipping described on news.t0.vc/TXJZ ("Current scope").
+    FIFO wait without skipping described on "6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference", section "Current scope".
     """
     rng = np.random.default_rng(seed)
     drawn = np.minimum(rng.geometric(1.0 / 256.0, size=requests), 2048).astype(np.int32)
