@@ -131,7 +131,9 @@ pkv_status pkv_kv_append(const pkv_pool *pool, const int32_t *block_tables, int3
  *                     pkv_plan_partition_pages for the current device.  When a sequence's
  *                     pages are cut into several partitions, each partition produces a
  *                     (max, sum, partial output) triple per query head in `workspace` and a
- *                     second kernel merges them; >= max_blocks_per_seq never splits.
+ *                     second kernel merges them.  Values above 256 are treated as 256 (one
+ *                     workgroup covers at most 256 pages); >= max_blocks_per_seq (when that is
+ *                     <= 256) never splits.
  *   workspace         device scratch of at least pkv_decode_workspace_bytes(...) bytes for the
  *                     resolved partition size (may be NULL when that is 0).  Contents on entry
  *                     are ignored; on return they are unspecified.
@@ -146,13 +148,14 @@ pkv_status pkv_paged_decode_attention(const void *q, const void *k_pool, const v
 /*
  * Pages per partition chosen when partition_pages <= 0.  Pure function (no GPU needed):
  * no split when batch * num_kv_heads workgroups already cover the device, otherwise the
- * smallest multiple of 4 pages (at least 4) that yields about 4 workgroups per compute unit.
- * Returns a value >= max_blocks_per_seq when no split is needed; -1 on bad arguments.
+ * smallest multiple of 4 pages (at least 4) that yields about 4 workgroups per compute unit;
+ * never more than 256.  Returns min(max_blocks_per_seq, 256) when no split is needed; -1 on bad
+ * arguments.
  */
 int32_t pkv_plan_partition_pages(int32_t batch, int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t num_cus);
 
-/* Workspace bytes needed for the given (resolved, positive) partition size; 0 without a split.
- * Returns 0 on bad arguments. */
+/* Workspace bytes needed for the given positive partition size (after the same 256-page cap
+ * the attention call applies); 0 without a split.  Returns 0 on bad arguments. */
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                   int32_t partition_pages);
 

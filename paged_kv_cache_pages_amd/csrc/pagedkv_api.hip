@@ -71,17 +71,29 @@ extern "C" int32_t pkv_plan_partition_pages(int32_t batch, int32_t num_kv_heads,
   if (batch < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_cus <= 0) return -1;
   const int64_t pairs = (int64_t)batch * num_kv_heads;
   const int64_t target = 4LL * num_cus;  // ~4 resident 4-wavefront workgroups per CU
-  if (pairs == 0 || 2 * pairs >= target) return max_blocks_per_seq;
+  const int32_t cap = max_blocks_per_seq < pkv::kMaxPartitionPages ? max_blocks_per_seq : pkv::kMaxPartitionPages;
+  if (pairs == 0 || 2 * pairs >= target) return cap;
   int64_t pages = ((int64_t)max_blocks_per_seq * pairs + target - 1) / target;
   pages = ((pages + 3) / 4) * 4;  // one page per wavefront at least, equal shares
   if (pages < 4) pages = 4;
-  return pages >= max_blocks_per_seq ? max_blocks_per_seq : (int32_t)pages;
+  return pages >= cap ? cap : (int32_t)pages;
 }
+
+namespace {
+// Pages per partition actually used for a requested (positive) size.
+int32_t resolved_partition_pages(int32_t requested, int32_t max_blocks_per_seq) {
+  int32_t pp = requested;
+  if (pp > max_blocks_per_seq) pp = max_blocks_per_seq;
+  if (pp > pkv::kMaxPartitionPages) pp = pkv::kMaxPartitionPages;
+  return pp;
+}
+}  // namespace
 
 extern "C" size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                              int32_t partition_pages) {
   if (batch < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_pages <= 0) return 0;
-  const int64_t parts = ((int64_t)max_blocks_per_seq + partition_pages - 1) / partition_pages;
+  const int32_t pp = resolved_partition_pages(partition_pages, max_blocks_per_seq);
+  const int64_t parts = ((int64_t)max_blocks_per_seq + pp - 1) / pp;
   if (parts <= 1) return 0;
   const int64_t slots = (int64_t)batch * num_q_heads * parts;
   return (size_t)slots * (pkv::kHeadDim + 2) * sizeof(float);
@@ -146,7 +158,7 @@ extern "C" pkv_status pkv_paged_decode_attention(const void *q, const void *k_po
     if (cus <= 0) return PKV_ERR_HIP;
     part_pages = pkv_plan_partition_pages(batch, num_kv_heads, max_blocks_per_seq, cus);
   }
-  if (part_pages > max_blocks_per_seq) part_pages = max_blocks_per_seq;
+  part_pages = resolved_partition_pages(part_pages, max_blocks_per_seq);
   const int32_t num_parts = (max_blocks_per_seq + part_pages - 1) / part_pages;
   if (num_parts > 1) {
     const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, max_blocks_per_seq, part_pages);

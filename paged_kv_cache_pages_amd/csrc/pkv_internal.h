@@ -11,6 +11,9 @@ namespace pkv {
 constexpr int kBlock = 16;
 constexpr int kHeadDim = 64;
 constexpr int kGroup = 4;
+// A decode workgroup has 4 wavefronts and each holds one block-table entry per lane, so one
+// partition covers at most 4 * 64 pages; longer tables are always split.
+constexpr int kMaxPartitionPages = 256;
 
 struct AppendParams {
   uint16_t *k_pool;
