@@ -117,7 +117,7 @@ def _dev_tensor(name, t, dtype, ndim=None):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
@@ -128,29 +128,58 @@ def _dev_tensor(name, t, dtype, ndim=None):
     return t
 
 
-def _stream_handle(stream):
+def _stream_handle(stream, device):
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
+    s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream
 
 
-def cu_count() -> int:
-    n = library().pkv_device_cu_count()
-    if n <= 0:
-        raise RuntimeError("no HIP device available")
-    return int(n)
+_cu_counts = {}
+_plans = {}
+_workspaces = {}
+
+
+def cu_count(device=None) -> int:
+    """Compute units of a device (queried once per device through the library)."""
+    torch = _torch()
+    idx = torch.cuda.current_device() if device is None else torch.device(device).index
+    n = _cu_counts.get(idx)
+    if n is None:
+        with torch.cuda.device(idx):
+            n = int(library().pkv_device_cu_count())
+        if n <= 0:
+            raise RuntimeError("no HIP device available")
+        _cu_counts[idx] = n
+    return n
 
 
 def plan_partition_pages(batch: int, num_kv_heads: int, max_blocks_per_seq: int, num_cus: int | None = None) -> int:
-    cus = cu_count() if num_cus is None else int(num_cus)
-    r = library().pkv_plan_partition_pages(batch, num_kv_heads, max_blocks_per_seq, cus)
-    if r <= 0:
-        raise ValueError("invalid planning arguments")
-    return int(r)
+    key = (batch, num_kv_heads, max_blocks_per_seq, num_cus)
+    r = _plans.get(key)
+    if r is None:
+        cus = cu_count() if num_cus is None else int(num_cus)
+        r = int(library().pkv_plan_partition_pages(batch, num_kv_heads, max_blocks_per_seq, cus))
+        if r <= 0:
+            raise ValueError("invalid planning arguments")
+        if num_cus is not None:
+            _plans[key] = r
+    return r
 
 
 def decode_workspace_bytes(batch: int, num_q_heads: int, max_blocks_per_seq: int, partition_pages: int) -> int:
     return int(library().pkv_decode_workspace_bytes(batch, num_q_heads, max_blocks_per_seq, partition_pages))
+
+
+def _cached_workspace(nbytes: int, device, stream_handle):
+    """A workspace tensor kept per (device, stream) and grown on demand.  Calls on one stream are
+    ordered, so reusing its workspace is safe; other streams get their own."""
+    torch = _torch()
+    key = (device.index, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
 
 
 # ---------------------------------------------------------------------------------------------
@@ -175,7 +204,7 @@ def kv_append(k_pool, v_pool, block_tables, positions, k_new, v_new, stream=None
     pool = Pool(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, hkv, dim, block)
     st = library().pkv_kv_append(
         ctypes.byref(pool), block_tables.data_ptr(), block_tables.shape[1], positions.data_ptr(), k_new.data_ptr(),
-        v_new.data_ptr(), batch, _stream_handle(stream),
+        v_new.data_ptr(), batch, _stream_handle(stream, k_pool.device),
     )
     _check("pkv_kv_append", st)
 
@@ -185,8 +214,8 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=No
     """Decode attention of q [B][Hq][D] over each sequence's pages; returns out [B][Hq][D].
 
     ``out_dtype`` is torch.bfloat16 (default) or torch.float32; ``scale`` defaults to
-    1/sqrt(head_dim).  ``partition_pages`` <= 0 lets the library plan the context split; the
-    partial-result workspace is allocated here through torch when none is passed.
+    1/sqrt(head_dim).  ``partition_pages`` <= 0 lets the library plan the context split; when no
+    workspace is passed, a torch buffer cached per (device, stream) is used.
     """
     torch = _torch()
     _dev_tensor("q", q, torch.bfloat16, 3)
@@ -212,18 +241,19 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=No
         scale = 1.0 / float(dim) ** 0.5
     pp = int(partition_pages)
     if pp <= 0:
-        pp = plan_partition_pages(batch, hkv, max_blocks)
+        pp = plan_partition_pages(batch, hkv, max_blocks, cu_count(q.device))
     need = decode_workspace_bytes(batch, hq, max_blocks, pp)
+    sh = _stream_handle(stream, q.device)
     ws_ptr, ws_bytes = None, 0
     if need > 0:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _cached_workspace(need, q.device, sh)
         _dev_tensor("workspace", workspace, workspace.dtype)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = library().pkv_paged_decode_attention(
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), num_pages, block_tables.data_ptr(), max_blocks,
         context_lens.data_ptr(), out.data_ptr(), PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32,
-        batch, hq, hkv, dim, block, float(scale), pp, ws_ptr, ws_bytes, _stream_handle(stream),
+        batch, hq, hkv, dim, block, float(scale), pp, ws_ptr, ws_bytes, sh,
     )
     _check("pkv_paged_decode_attention", st)
     return out

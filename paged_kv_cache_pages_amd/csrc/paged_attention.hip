@@ -367,38 +367,66 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
 }
 
 // Combine the partitions of one (sequence, query head): M = max m_i, O = sum o_i 2^(m_i - M),
-// l = sum l_i 2^(m_i - M), out = O / l.  The sequence's table row is re-validated here, so an
-// invalid entry anywhere zeroes the row exactly as the unsplit kernel does.
+// l = sum l_i 2^(m_i - M), out = O / l.  One wavefront: the partitions' (m, l) pairs are spread
+// over the lanes (64 at a time) for the max and the weighted sum; then lane d accumulates dim d of
+// the partial outputs with the weights broadcast from the lanes that hold them.  The sequence's
+// table row is re-validated here, so an invalid entry anywhere zeroes the row exactly as the
+// unsplit kernel does.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmax_plain(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 template <bool kOutBf16>
 __global__ __launch_bounds__(64) void merge_partitions_kernel(DecodeParams p) {
   const int b = blockIdx.x / p.num_q_heads;
   const int h = blockIdx.x % p.num_q_heads;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x;
   const int L = p.context_lens[b];
   const bool len_ok = L > 0 && L <= p.max_blocks * kBlock;
   const int n_pages = len_ok ? (L + kBlock - 1) / kBlock : 0;
   bool bad = false;
   const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
-  for (int i = d; i < n_pages; i += 64) {
+  for (int i = lane; i < n_pages; i += 64) {
     const int id = bt[i];
     bad |= id < 0 || id >= p.num_pages;
   }
-  bad = __any(bad);
+  bad = __builtin_amdgcn_ballot_w64(bad) != 0;
   float r = 0.0f;
   if (len_ok && !bad) {
     const int n_parts = (n_pages + p.part_pages - 1) / p.part_pages;
     const int64_t slot0 = ((int64_t)b * p.num_q_heads + h) * p.num_parts;
+    const float *ml = p.part_ml + slot0 * 2;
+    const float *po = p.part_o + slot0 * kHeadDim + lane;
     float M = -INFINITY;
-    for (int i = 0; i < n_parts; ++i) M = fmax_plain(M, p.part_ml[(slot0 + i) * 2]);
-    float O = 0.0f, Ls = 0.0f;
-    for (int i = 0; i < n_parts; ++i) {
-      const float e = __builtin_amdgcn_exp2f(p.part_ml[(slot0 + i) * 2] - M);
-      O = __builtin_fmaf(e, p.part_o[(slot0 + i) * kHeadDim + d], O);
-      Ls = __builtin_fmaf(e, p.part_ml[(slot0 + i) * 2 + 1], Ls);
+    for (int i0 = 0; i0 < n_parts; i0 += 64) {
+      const int i = i0 + lane;
+      M = fmax_plain(M, i < n_parts ? ml[2 * i] : -INFINITY);
     }
-    r = O / Ls;
+    M = wave_max(M);
+    float O = 0.0f, Ls = 0.0f;
+    for (int i0 = 0; i0 < n_parts; i0 += 64) {
+      const int i = i0 + lane;
+      const float e = i < n_parts ? __builtin_amdgcn_exp2f(ml[2 * i] - M) : 0.0f;
+      Ls += i < n_parts ? e * ml[2 * i + 1] : 0.0f;
+      const int cnt = min(64, n_parts - i0);
+      const int eb = __builtin_bit_cast(int, e);
+#pragma unroll 8
+      for (int j = 0; j < cnt; ++j) {
+        const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, j));
+        O = __builtin_fmaf(ej, po[(int64_t)(i0 + j) * kHeadDim], O);
+      }
+    }
+    r = O / wave_sum(Ls);
   }
-  const int64_t o = ((int64_t)b * p.num_q_heads + h) * kHeadDim + d;
+  const int64_t o = ((int64_t)b * p.num_q_heads + h) * kHeadDim + lane;
   if (kOutBf16) static_cast<uint16_t *>(p.out)[o] = f32_to_bf16_rne(r);
   else static_cast<float *>(p.out)[o] = r;
 }
