@@ -71,12 +71,17 @@ __device__ __forceinline__ float sum8(float x) {
 
 __device__ __forceinline__ float fmax_plain(float a, float b) { return a > b ? a : b; }
 
-// Maximum over the whole wavefront of a value that is already uniform within 8-lane groups.
+// Maximum over the whole wavefront of a value that is already uniform within 8-lane groups:
+// fold the two groups of each 16-lane row with DPP, then take the four rows' values with
+// readlane (no LDS permute).  The result is wave-uniform.
 __device__ __forceinline__ float wave_max_of_groups(float x) {
   x = fmax_plain(x, dpp<kRowRor8>(x));
-  x = fmax_plain(x, __shfl_xor(x, 16));
-  x = fmax_plain(x, __shfl_xor(x, 32));
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+  const int b = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return fmax_plain(fmax_plain(r0, r1), fmax_plain(r2, r3));
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -418,7 +423,6 @@ __global__ __launch_bounds__(64) void merge_partitions_kernel(DecodeParams p) {
       Ls += i < n_parts ? e * ml[2 * i + 1] : 0.0f;
       const int cnt = min(64, n_parts - i0);
       const int eb = __builtin_bit_cast(int, e);
-#pragma unroll 8
       for (int j = 0; j < cnt; ++j) {
         const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, j));
         O = __builtin_fmaf(ej, po[(int64_t)(i0 + j) * kHeadDim], O);
