@@ -17,3 +17,4 @@ from .paged_oracle import (  # noqa: F401
     paged_decode_attention,
     softmax_two_pass,
 )
+from .rope_oracle import bf16_bits_to_f32, rope_kv_append, rope_pair_index, rope_rotate  # noqa: F401,E402

@@ -24,6 +24,7 @@ from .configs import (  # noqa: F401
     NUM_Q_HEADS,
     Workload,
     f32_to_bf16_bits,
+    llama3_rope_tables,
     make_config,
     make_custom,
     normal_bf16,

@@ -295,3 +295,28 @@ def make_custom(
         tables[:, nonempty, :] = sub
     rows = _draw_rows(rng, layers, len(lengths), num_pages, num_kv_heads * group, num_kv_heads, head_dim)
     return _finish("custom", seed, tables, lengths, rows, {"sum_context": int(lengths.sum())})
+
+
+def llama3_rope_tables(max_pos: int, head_dim: int = HEAD_DIM, theta: float = 500000.0, factor: float = 32.0,
+                       low_freq_factor: float = 1.0, high_freq_factor: float = 4.0, original_context: int = 8192):
+    """FP32 cos/sin tables [max_pos][head_dim] for the rotary embedding, built the way Llama-3
+    checkpoints specify their frequencies (base theta plus the piecewise long-context scaling).
+
+    Input construction only.  The pages do not print how their engine fills these tables (only
+    that it fills them once at start-up, and that the two slots of each rotated pair hold the same
+    value, "The prefill path: flowing the entire prompt at once", section "RoPE: a rotation that
+    references a table"), so the tables are caller inputs of the rotation; this builder gives
+    realistic values.  Entry [pos][2i] and [pos][2i+1] both hold the angle of pair i.
+    """
+    half = head_dim // 2
+    inv = 1.0 / theta ** (np.arange(half, dtype=np.float64) * 2.0 / head_dim)
+    wavelen = 2.0 * np.pi / inv
+    low_wl = original_context / low_freq_factor
+    high_wl = original_context / high_freq_factor
+    smooth = (original_context / wavelen - low_freq_factor) / (high_freq_factor - low_freq_factor)
+    scaled = np.where(wavelen > low_wl, inv / factor, inv)
+    mid = (wavelen <= low_wl) & (wavelen >= high_wl)
+    scaled = np.where(mid, (1.0 - smooth) * inv / factor + smooth * inv, scaled)
+    angles = np.arange(max_pos, dtype=np.float64)[:, None] * scaled[None, :]  # [pos][half]
+    full = np.repeat(angles, 2, axis=1)  # slots 2i and 2i+1 share pair i's angle
+    return np.cos(full).astype(np.float32), np.sin(full).astype(np.float32)
