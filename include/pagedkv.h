@@ -108,6 +108,32 @@ pkv_status pkv_kv_append(const pkv_pool *pool, const int32_t *block_tables, int3
                          void *stream);
 
 /*
+ * rope_kv_append: the decode step's rotary embedding fused into kv_append.
+ *
+ * For every sequence b at absolute position pos = positions[b]: rotate each query head of
+ * q[b] and the new key row k_new[b][g] ("The prefill path: flowing the entire prompt at once",
+ * section "RoPE: a rotation that references a table": inside each 64-wide head, element i is
+ * paired with element i + 32 and rotated by the angle of slot 2i of the position's table row:
+ *   y_i = x_i * c - x_{i+32} * s,   y_{i+32} = x_i * s + x_{i+32} * c,
+ * with c = cos_table[pos][2i], s = sin_table[pos][2i]; every product and the sum/difference are
+ * separate FP32 operations, the result is rounded to BF16 to nearest even).  The rotated query
+ * goes to q_out; the rotated key and the unrotated v_new[b][g] are written into the pool exactly
+ * as pkv_kv_append writes them.  Values are not rotated.
+ *
+ *   q, q_out            device bf16[batch][num_q_heads][64]; q_out may equal q (in place)
+ *   k_new, v_new        device bf16[batch][num_kv_heads][64]; not modified
+ *   cos_table, sin_table device f32[table_rows][64], built by the caller (e.g. with the model's
+ *                       RoPE frequencies); slots 2i and 2i+1 conventionally hold the same value
+ * A sequence whose position is outside [0, table_rows), outside the block table or whose page
+ * entry is out of range is skipped entirely: its q_out rows and its pool slots are not written.
+ * With PKV_DEBUG_VALIDATE=1 such a batch is rejected with PKV_ERR_VALIDATION instead.
+ */
+pkv_status pkv_rope_kv_append(const pkv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                              const int32_t *positions, const void *q, void *q_out, int32_t num_q_heads,
+                              const void *k_new, const void *v_new, const float *cos_table,
+                              const float *sin_table, int32_t table_rows, int32_t batch, void *stream);
+
+/*
  * paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out)
  *
  * For every sequence b, query head h (KV head g = h / 4) and dim d:

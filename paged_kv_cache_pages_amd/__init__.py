@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     paged_decode_attention,
     plan_partition_pages,
     require_library,
+    rope_kv_append,
     validate_append_host,
     validate_decode_host,
 )

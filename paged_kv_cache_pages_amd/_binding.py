@@ -54,6 +54,10 @@ SIGNATURES = {
         [_vp, _vp, _vp, _c_int32, _vp, _c_int32, _vp, _vp, ctypes.c_int, _c_int32, _c_int32, _c_int32, _c_int32,
          _c_int32, ctypes.c_float, _c_int32, _vp, _c_size, _vp],
     ),
+    "pkv_rope_kv_append": (
+        ctypes.c_int,
+        [ctypes.POINTER(Pool), _vp, _c_int32, _vp, _vp, _vp, _c_int32, _vp, _vp, _vp, _vp, _c_int32, _c_int32, _vp],
+    ),
     "pkv_plan_partition_pages": (_c_int32, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "pkv_decode_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "pkv_device_cu_count": (_c_int32, []),
@@ -207,6 +211,42 @@ def kv_append(k_pool, v_pool, block_tables, positions, k_new, v_new, stream=None
         v_new.data_ptr(), batch, _stream_handle(stream, k_pool.device),
     )
     _check("pkv_kv_append", st)
+
+
+def rope_kv_append(k_pool, v_pool, block_tables, positions, q, k_new, v_new, cos_table, sin_table, q_out=None,
+                   stream=None):
+    """Rotate q and k_new at each sequence's position (tables [rows][64] float32), write the
+    rotated key and v_new into the pool; returns the rotated q (``q_out``, which may be ``q``)."""
+    torch = _torch()
+    _dev_tensor("k_pool", k_pool, torch.bfloat16, 4)
+    _dev_tensor("v_pool", v_pool, torch.bfloat16, 4)
+    _dev_tensor("block_tables", block_tables, torch.int32, 2)
+    _dev_tensor("positions", positions, torch.int32, 1)
+    _dev_tensor("q", q, torch.bfloat16, 3)
+    _dev_tensor("k_new", k_new, torch.bfloat16, 3)
+    _dev_tensor("v_new", v_new, torch.bfloat16, 3)
+    _dev_tensor("cos_table", cos_table, torch.float32, 2)
+    _dev_tensor("sin_table", sin_table, torch.float32, 2)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _dev_tensor("q_out", q_out, torch.bfloat16, 3)
+    num_pages, hkv, block, dim = k_pool.shape
+    batch, hq, _ = q.shape
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(q_out.shape) != tuple(q.shape):
+        raise ValueError("inconsistent pool / q shapes")
+    if positions.shape[0] != batch or block_tables.shape[0] != batch or tuple(k_new.shape) != (batch, hkv, dim) \
+            or k_new.shape != v_new.shape:
+        raise ValueError("inconsistent batch / head shapes")
+    if tuple(cos_table.shape) != tuple(sin_table.shape) or cos_table.shape[1] != dim:
+        raise ValueError("cos/sin tables must both be [rows][head_dim]")
+    pool = Pool(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, hkv, dim, block)
+    st = library().pkv_rope_kv_append(
+        ctypes.byref(pool), block_tables.data_ptr(), block_tables.shape[1], positions.data_ptr(), q.data_ptr(),
+        q_out.data_ptr(), hq, k_new.data_ptr(), v_new.data_ptr(), cos_table.data_ptr(), sin_table.data_ptr(),
+        cos_table.shape[0], batch, _stream_handle(stream, k_pool.device),
+    )
+    _check("pkv_rope_kv_append", st)
+    return q_out
 
 
 def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=None, *, out_dtype=None, scale=None,

@@ -134,6 +134,55 @@ extern "C" pkv_status pkv_kv_append(const pkv_pool *pool, const int32_t *block_t
   return pkv::launch_kv_append(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+extern "C" pkv_status pkv_rope_kv_append(const pkv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t *positions, const void *q, void *q_out, int32_t num_q_heads,
+                                         const void *k_new, const void *v_new, const float *cos_table,
+                                         const float *sin_table, int32_t table_rows, int32_t batch, void *stream) {
+  if (!pool) return PKV_ERR_NULL;
+  if (batch < 0 || max_blocks_per_seq <= 0 || pool->num_pages <= 0 || pool->num_kv_heads <= 0 || num_q_heads <= 0 ||
+      table_rows <= 0)
+    return PKV_ERR_SHAPE;
+  if (pool->head_dim != pkv::kHeadDim || pool->block_size != pkv::kBlock) return PKV_ERR_UNSUPPORTED;
+  if (batch == 0) return PKV_OK;
+  if (!pool->k_pool || !pool->v_pool || !block_tables || !positions || !q || !q_out || !k_new || !v_new ||
+      !cos_table || !sin_table)
+    return PKV_ERR_NULL;
+  if (!aligned16(pool->k_pool) || !aligned16(pool->v_pool) || !aligned16(q) || !aligned16(q_out) ||
+      !aligned16(k_new) || !aligned16(v_new) || !aligned16(cos_table) || !aligned16(sin_table))
+    return PKV_ERR_ALIGNMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (debug_validate_enabled()) {
+    std::vector<int32_t> bt, pos;
+    pkv_status st = copy_to_host(bt, block_tables, (size_t)batch * max_blocks_per_seq, s);
+    if (st == PKV_OK) st = copy_to_host(pos, positions, (size_t)batch, s);
+    if (st != PKV_OK) return st;
+    st = pkv_validate_append_host(bt.data(), max_blocks_per_seq, pos.data(), batch, pool->num_pages, nullptr);
+    if (st != PKV_OK) return st;
+    for (int32_t b = 0; b < batch; ++b)
+      if (pos[b] >= table_rows) return PKV_ERR_VALIDATION;
+  }
+
+  pkv::RopeAppendParams p;
+  p.app.k_pool = static_cast<uint16_t *>(pool->k_pool);
+  p.app.v_pool = static_cast<uint16_t *>(pool->v_pool);
+  p.app.block_tables = block_tables;
+  p.app.positions = positions;
+  p.app.k_new = static_cast<const uint16_t *>(k_new);
+  p.app.v_new = static_cast<const uint16_t *>(v_new);
+  p.app.num_pages = pool->num_pages;
+  p.app.num_kv_heads = pool->num_kv_heads;
+  p.app.max_blocks = max_blocks_per_seq;
+  p.app.batch = batch;
+  p.q = static_cast<const uint16_t *>(q);
+  p.q_out = static_cast<uint16_t *>(q_out);
+  p.cos_table = cos_table;
+  p.sin_table = sin_table;
+  p.table_rows = table_rows;
+  p.num_q_heads = num_q_heads;
+  return pkv::launch_rope_append(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 extern "C" pkv_status pkv_paged_decode_attention(const void *q, const void *k_pool, const void *v_pool,
                                                  int32_t num_pages, const int32_t *block_tables,
                                                  int32_t max_blocks_per_seq, const int32_t *context_lens, void *out,

@@ -47,7 +47,18 @@ struct DecodeParams {
   float score_log2;    // scale * log2(e): scores are kept in log2 units so exp2 does the softmax
 };
 
+struct RopeAppendParams {
+  AppendParams app;       // pools, tables, positions, k_new (rotated on the way), v_new
+  const uint16_t *q;      // [batch][num_q_heads][kHeadDim]
+  uint16_t *q_out;        // rotated q (may equal q)
+  const float *cos_table; // [table_rows][kHeadDim]
+  const float *sin_table;
+  int32_t table_rows;
+  int32_t num_q_heads;
+};
+
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
+hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeParams &p, bool out_bf16, hipStream_t stream);
 
 }  // namespace pkv

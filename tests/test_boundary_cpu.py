@@ -111,6 +111,24 @@ def test_decode_host_checks(lib):
     assert _decode(lib, pp=4, ws=FAKE + 8, wsb=need) == ALIGN
 
 
+def test_rope_append_host_checks(lib):
+    good = pkv.Pool(FAKE, FAKE, 8, 8, 64, 16)
+
+    def call(pool=ctypes.byref(good), q=FAKE, q_out=FAKE, hq=32, cos=FAKE, sin=FAKE, rows=16, batch=1):
+        return lib.pkv_rope_kv_append(pool, FAKE, 128, FAKE, q, q_out, hq, FAKE, FAKE, cos, sin, rows, batch, None)
+
+    assert call(pool=None) == NULL
+    assert call(rows=0) == SHAPE
+    assert call(hq=0) == SHAPE
+    assert call(batch=-1) == SHAPE
+    assert call(pool=ctypes.byref(pkv.Pool(FAKE, FAKE, 8, 8, 32, 16))) == UNSUP
+    assert call(batch=0) == OK
+    assert call(cos=None) == NULL
+    assert call(q_out=None) == NULL
+    assert call(sin=FAKE + 4) == ALIGN
+    assert call(q=FAKE + 2) == ALIGN
+
+
 def test_host_validators():
     bt = np.full((3, 4), -1, dtype=np.int32)
     bt[0, :2] = [5, 6]
