@@ -81,14 +81,14 @@ def kernel_source_digest() -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def recorded_traffic():
-    """Traffic per launch from the committed counter summary, or None when the kernel source has
-    changed since the counters were taken."""
+def recorded_traffic(tag: str):
+    """Traffic per launch of the ``tag`` kernel ("attention" or "fused") from the committed counter
+    summary, or None when the kernel source has changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_PROFILE):
         return None
     text = open(TRAFFIC_PROFILE).read()
     m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch\[" + tag + r"\]:\s*([0-9.eE+]+)", text)
     if not (m_src and m_val) or m_src.group(1) != kernel_source_digest():
         return None
     return float(m_val.group(1))
@@ -197,43 +197,46 @@ def run(args):
             pkv.paged_decode_attention(t["q"], kp, vp, t["bt"], lens, t["out"], partition_pages=pp,
                                        workspace=workspace)
 
-    for _ in range(args.warmup):
-        append_all()
-        attend_all()
-    torch.cuda.synchronize()
+    def fused_all():
+        for t in layers:
+            pkv.decode_step(t["q"], kp, vp, t["bt"], pos, t["k_new"], t["v_new"], t["out"], partition_pages=pp,
+                            workspace=workspace)
 
     K = args.steps
-    # Per-launch kernel durations: HIP events around each call on the stream the library
-    # launches on (torch's current stream, which the binding passes down).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record()
-        append_all()
-        ev[i][1].record()
-        attend_all()
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    append_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
 
-    if args.graph:
-        # The whole step (every layer's append and attention) captured once as a HIP graph and
-        # replayed: same kernels and bytes, no per-launch host work.  The step time becomes the
-        # graph replay's wall time; the per-launch kernel times above stay the roofline input.
+    def timed(phases):
+        """Run K steps made of ``phases`` (callables, run in order); HIP events on the launch stream
+        bracket every phase.  Returns (wall seconds for K steps, per-phase mean ms)."""
+        for _ in range(args.warmup):
+            for f in phases:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            for j, f in enumerate(phases):
+                ev[i][j].record()
+                f()
+            ev[i][len(phases)].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(len(phases))]
+
+    def graph_wall(phases):
+        """The whole step captured once as a HIP graph and replayed K times: same kernels and
+        bytes, no per-launch host work."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            append_all()
-            attend_all()
+            for f in phases:
+                f()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            append_all()
-            attend_all()
+            for f in phases:
+                f()
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
@@ -241,7 +244,16 @@ def run(args):
         for _ in range(K):
             graph.replay()
         torch.cuda.synchronize()
-        wall_s = time.perf_counter() - t0
+        return time.perf_counter() - t0
+
+    # Both forms of the step do the same work: every layer's append, then its attention over the
+    # context including the appended token.  "two-call" uses pkv_kv_append + pkv_paged_decode_
+    # attention; "fused" uses pkv_decode_step, one launch per layer that also writes the new rows.
+    two_wall, (append_ms, attn_ms) = timed([append_all, attend_all])
+    fused_wall, (fused_ms,) = timed([fused_all])
+    if args.graph:
+        two_wall = graph_wall([append_all, attend_all])
+        fused_wall = graph_wall([fused_all])
 
     # plain device-to-device copy of 1 GiB (2 GiB moved) as an achievable-bandwidth reference
     src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
@@ -256,14 +268,29 @@ def run(args):
     copy_gbps = 5 * 2 * src.numel() * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    ms_per_step = wall_s * 1e3 / K
     a_bytes, p_bytes = attention_bytes(w), append_bytes(w)
     step_bytes = a_bytes + p_bytes
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    # one "launch" of the attention kernel = one layer's decode attention
-    attn_launch_ms = float(np.mean(attn_ms)) / w.layers
-    attn_gbps = (a_bytes / w.layers) / (attn_launch_ms * 1e-3) / 1e9
-    traffic = recorded_traffic() if pp >= w.max_blocks and args.config == "bw256" else None
+    gbps = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    two_ms = two_wall * 1e3 / K
+    fused_msps = fused_wall * 1e3 / K
+    fused_mode = args.step == "fused"
+    ms_per_step = fused_msps if fused_mode else two_ms
+    value = gbps(step_bytes, ms_per_step)
+    # One "launch" = one layer.  Dominant kernel: the fused decode kernel (attention + append
+    # bytes) or, for the two-call step, the attention kernel (attention bytes).
+    if fused_mode:
+        launch_ms = fused_ms / w.layers
+        launch_bytes = step_bytes // w.layers
+        kernel = "paged_decode_kernel (fused append)"
+    else:
+        launch_ms = attn_ms / w.layers
+        launch_bytes = a_bytes // w.layers
+        kernel = "paged_decode_kernel"
+    if pp < w.max_blocks:
+        kernel += " + merge_partitions_kernel"
+    achieved = gbps(launch_bytes, launch_ms)
+    traffic = recorded_traffic("fused" if fused_mode else "attention") \
+        if pp >= w.max_blocks and args.config == "bw256" else None
 
     result = {
         "metric": METRIC,
@@ -278,6 +305,8 @@ def run(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "compute": "bf16 inputs, f32 accumulate and softmax",
+        "step": "fused: pkv_decode_step, one launch per layer" if fused_mode
+                else "two-call: pkv_kv_append + pkv_paged_decode_attention per layer",
         "launch": "hip graph replay of the whole step" if args.graph else "eager launches through the C ABI",
         "data": "synthetic (seeded N(0,1) BF16; no dataset)",
         "config": {
@@ -295,18 +324,21 @@ def run(args):
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "seq_tokens_per_s": round(seq_tokens(w) / (ms_per_step * 1e-3), 1),
         "bytes_per_step": step_bytes,
-        "attention_us_per_launch": round(attn_launch_ms * 1e3, 3),
-        "append_us_per_step": round(float(np.mean(append_ms)) * 1e3, 3),
+        "fused": {"ms_per_step": round(fused_msps, 5), "us_per_launch": round(fused_ms / w.layers * 1e3, 3),
+                  "value": round(gbps(step_bytes, fused_msps), 2)},
+        "two_call": {"ms_per_step": round(two_ms, 5), "attention_us_per_launch": round(attn_ms / w.layers * 1e3, 3),
+                     "append_us_per_step": round(append_ms * 1e3, 3), "value": round(gbps(step_bytes, two_ms), 2),
+                     "attention_gbps": round(gbps(a_bytes / w.layers, attn_ms / w.layers), 2)},
         "copy_d2d_gbps": round(copy_gbps, 1),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(attn_gbps, 2),
+            "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "paged_decode_kernel" + ("" if pp >= w.max_blocks else " + merge_partitions_kernel"),
-            "algorithmic_bytes_per_launch": a_bytes // w.layers,
+            "kernel": kernel,
+            "algorithmic_bytes_per_launch": launch_bytes,
         },
         "note": "The reference pages report no throughput or hardware numbers for this kernel; "
                 "figures are this build's measurements on one MI355X.",
@@ -326,6 +358,8 @@ def main():
     ap.add_argument("--partition-pages", type=int, default=0, help="<= 0: library plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time the step as one captured HIP graph")
+    ap.add_argument("--step", choices=["fused", "two-call"], default="fused",
+                    help="which form of the step gives value/roofline (both are timed and reported)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0, help="repeat CPU oracle passes at least this long")
     ap.add_argument("--cpu-max-seconds", type=float, default=30.0, help="hard bound on the CPU oracle timing")
     args = ap.parse_args()

@@ -172,6 +172,27 @@ pkv_status pkv_paged_decode_attention(const void *q, const void *k_pool, const v
                                       size_t workspace_bytes, void *stream);
 
 /*
+ * decode_step: kv_append followed by paged_decode_attention over context = positions[b] + 1, in
+ * one launch.  The result (pool contents and out) is exactly that of pkv_kv_append(pool,
+ * block_tables, positions, k_new, v_new) then pkv_paged_decode_attention(..., context_lens =
+ * positions + 1, ...) with the same partition size.  The workgroup that reads a sequence's last
+ * page writes the new rows into the pool and uses them from registers, so this also holds when
+ * the old slot content is stale or NaN.
+ *
+ *   pool, block_tables, positions, k_new, v_new   as for pkv_kv_append
+ *   q, out, out_dtype, scale, partition_pages, workspace   as for pkv_paged_decode_attention
+ *   num_q_heads                                   4 * pool->num_kv_heads
+ * A position outside [0, 16 * max_blocks_per_seq) or a needed table entry outside [0, num_pages)
+ * appends nothing and zeroes that sequence's output rows, as the two separate calls would.
+ * Precondition (as for the separate calls): no other sequence of the batch references the page
+ * a sequence appends to.
+ */
+pkv_status pkv_decode_step(const pkv_pool *pool, const void *q, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *positions, const void *k_new, const void *v_new, void *out,
+                           pkv_out_dtype out_dtype, int32_t batch, int32_t num_q_heads, float scale,
+                           int32_t partition_pages, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Pages per partition chosen when partition_pages <= 0.  Pure function (no GPU needed):
  * no split when batch * num_kv_heads workgroups already cover the device, otherwise the
  * smallest multiple of 4 pages (at least 4) that yields about 4 workgroups per compute unit;

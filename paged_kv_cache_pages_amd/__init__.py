@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     PagedKVError,
     Pool,
     cu_count,
+    decode_step,
     decode_workspace_bytes,
     kv_append,
     library,

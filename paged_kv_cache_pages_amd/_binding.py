@@ -58,6 +58,11 @@ SIGNATURES = {
         ctypes.c_int,
         [ctypes.POINTER(Pool), _vp, _c_int32, _vp, _vp, _vp, _c_int32, _vp, _vp, _vp, _vp, _c_int32, _c_int32, _vp],
     ),
+    "pkv_decode_step": (
+        ctypes.c_int,
+        [ctypes.POINTER(Pool), _vp, _vp, _c_int32, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int32, _c_int32,
+         ctypes.c_float, _c_int32, _vp, _c_size, _vp],
+    ),
     "pkv_plan_partition_pages": (_c_int32, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "pkv_decode_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "pkv_device_cu_count": (_c_int32, []),
@@ -296,6 +301,56 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=No
         batch, hq, hkv, dim, block, float(scale), pp, ws_ptr, ws_bytes, sh,
     )
     _check("pkv_paged_decode_attention", st)
+    return out
+
+
+def decode_step(q, k_pool, v_pool, block_tables, positions, k_new, v_new, out=None, *, out_dtype=None, scale=None,
+                partition_pages: int = 0, workspace=None, stream=None):
+    """kv_append then decode attention over positions + 1 tokens, in one launch; returns out."""
+    torch = _torch()
+    _dev_tensor("q", q, torch.bfloat16, 3)
+    _dev_tensor("k_pool", k_pool, torch.bfloat16, 4)
+    _dev_tensor("v_pool", v_pool, torch.bfloat16, 4)
+    _dev_tensor("block_tables", block_tables, torch.int32, 2)
+    _dev_tensor("positions", positions, torch.int32, 1)
+    _dev_tensor("k_new", k_new, torch.bfloat16, 3)
+    _dev_tensor("v_new", v_new, torch.bfloat16, 3)
+    batch, hq, dim = q.shape
+    num_pages, hkv, block, _ = k_pool.shape
+    if tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_pool and v_pool shapes differ")
+    if block_tables.shape[0] != batch or positions.shape[0] != batch:
+        raise ValueError("block_tables / positions batch differs from q")
+    if tuple(k_new.shape) != (batch, hkv, dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new / v_new must be [batch][kv_heads][head_dim]")
+    max_blocks = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((batch, hq, dim), dtype=out_dtype or torch.bfloat16, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _dev_tensor("out", out, out.dtype, 3)
+    if tuple(out.shape) != (batch, hq, dim):
+        raise ValueError("out shape differs from q")
+    if scale is None:
+        scale = 1.0 / float(dim) ** 0.5
+    pp = int(partition_pages)
+    if pp <= 0:
+        pp = plan_partition_pages(batch, hkv, max_blocks, cu_count(q.device))
+    need = decode_workspace_bytes(batch, hq, max_blocks, pp)
+    sh = _stream_handle(stream, q.device)
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = _cached_workspace(need, q.device, sh)
+        _dev_tensor("workspace", workspace, workspace.dtype)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    pool = Pool(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, hkv, dim, block)
+    st = library().pkv_decode_step(
+        ctypes.byref(pool), q.data_ptr(), block_tables.data_ptr(), max_blocks, positions.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), out.data_ptr(), PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32, batch, hq,
+        float(scale), pp, ws_ptr, ws_bytes, sh,
+    )
+    _check("pkv_decode_step", st)
     return out
 
 

@@ -200,7 +200,16 @@ __device__ __forceinline__ void load_page(PageRegs &r, const uint16_t *kbase, co
   r.vb = load16_stream(vbase + off + 512);
 }
 
-template <bool kSplit, bool kOutBf16>
+// Context length of sequence b: context_lens[b], or, for the fused decode step, positions[b] + 1
+// (a position outside the block table gives an invalid length, hence a zero output row).
+template <bool kFused>
+__device__ __forceinline__ int context_length(const DecodeParams &p, int b) {
+  if (!kFused) return p.context_lens[b];
+  const int pos = p.positions[b];
+  return (pos >= 0 && pos < p.max_blocks * kBlock) ? pos + 1 : -1;
+}
+
+template <bool kSplit, bool kOutBf16, bool kFused>
 __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) {
   __shared__ float s_acc[kWaves][4][kGroup][kHeadDim];  // [wave][16-lane row][head][dim]
   __shared__ float s_l[kWaves][4][kGroup];
@@ -215,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   const int b = pair / p.num_kv_heads;
   const int qh0 = g * kGroup;  // first query head of the group
 
-  const int L = p.context_lens[b];
+  const int L = context_length<kFused>(p, b);
   const bool len_ok = L >= 0 && L <= p.max_blocks * kBlock;
   const int n_pages = len_ok ? (L + kBlock - 1) / kBlock : 0;
   const int p0 = part * p.part_pages;
@@ -252,6 +261,14 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   const int ids = lane < n_w ? bt[(int64_t)kWaves * lane] : 0;
   const bool bad = __builtin_amdgcn_ballot_w64(ids < 0 || ids >= p.num_pages) != 0;
   if (bad) n_w = 0;
+  // The wavefront holding the sequence's last page (it always holds the new token).
+  const bool owns_last = n_w > 0 && p1 == n_pages && p0 + wave + kWaves * (n_w - 1) == n_pages - 1;
+  uint4 knew = make_uint4(0u, 0u, 0u, 0u), vnew = knew;
+  if (kFused && owns_last) {
+    const int64_t row = ((int64_t)b * p.num_kv_heads + g) * kHeadDim + chunk * 8;
+    knew = load16(p.k_new + row);
+    vnew = load16(p.v_new + row);
+  }
   // q and the table entries must have landed before the first page load is issued (the page
   // addresses need the entries anyway).  Waiting here explicitly also tells the compiler that q
   // is resident inside the page loop, so the loop's waits only count the page loads in flight.
@@ -273,11 +290,36 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   const uint16_t *vbase = p.v_pool + g * head_elems + lane * 8;
   auto page_off = [&](int k) -> int64_t { return (int64_t)__builtin_amdgcn_readlane(ids, k) * page_elems; };
 
-  // The sequence's last page is partial when L % 16 != 0; the wavefront that owns it takes it
-  // first (outside the pipelined loop), so the loop below only ever sees full pages.
+  // The sequence's last page can be partial (L % 16 != 0) and, in the fused step, receives the
+  // new token.  The wavefront that owns it always takes it first, outside the pipelined loop, so
+  // the loop only sees ordinary full pages and the fused and unfused kernels add up the pages in
+  // the same order (their results are bit-identical).
   const int tail_valid = L - (n_pages - 1) * kBlock;
-  const bool own_partial = n_w > 0 && tail_valid < kBlock && p1 == n_pages && p0 + wave + kWaves * (n_w - 1) == n_pages - 1;
+  const bool own_partial = owns_last;
   const int n_full = own_partial ? n_w - 1 : n_w;
+  if (kFused && own_partial) {
+    // Append: the 8 lanes that hold the new token's slot write its K and V rows (16 B each) into
+    // the pool.  The same rows replace that slot in registers below, so the attention never
+    // depends on when these stores become visible.
+    const int slot = tail_valid - 1;  // position % 16
+    if (tok == (slot & 7)) {
+      const int64_t dst = ((int64_t)__builtin_amdgcn_readlane(ids, n_w - 1) * p.num_kv_heads + g) * (kBlock * kHeadDim) +
+                          slot * kHeadDim + chunk * 8;
+      *reinterpret_cast<uint4 *>(p.k_pool_w + dst) = knew;
+      *reinterpret_cast<uint4 *>(p.v_pool_w + dst) = vnew;
+    }
+  }
+  // Swap the new token's row into the last page's registers (fused step only).
+  auto with_new_token = [&](PageRegs r) -> PageRegs {
+    if (kFused) {
+      const int slot = tail_valid - 1;
+      const bool hi = slot >= 8;
+      const bool mine = tok == (slot & 7);
+      if (mine && !hi) { r.ka = knew; r.va = vnew; }
+      if (mine && hi) { r.kb = knew; r.vb = vnew; }
+    }
+    return r;
+  };
 
   // Three page buffers: two pages in flight while one is computed.  The pipelined loop is only
   // entered from a path where both prefetches were issued unconditionally and it only runs while
@@ -289,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   if (n_full >= 5) {
     load_page(b0, kbase, vbase, page_off(0));
     load_page(b1, kbase, vbase, page_off(1));
-    if (own_partial) process_page<true>(st, qv, b2, tok, tail_valid, c_log2);
+    if (own_partial) process_page<true>(st, qv, with_new_token(b2), tok, tail_valid, c_log2);
     for (; k + 4 < n_full; k += 3) {
       load_page(b2, kbase, vbase, page_off(k + 2));
       process_page<false>(st, qv, b0, tok, kBlock, c_log2);
@@ -301,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   } else {
     if (n_full > 0) load_page(b0, kbase, vbase, page_off(0));
     if (n_full > 1) load_page(b1, kbase, vbase, page_off(1));
-    if (own_partial) process_page<true>(st, qv, b2, tok, tail_valid, c_log2);
+    if (own_partial) process_page<true>(st, qv, with_new_token(b2), tok, tail_valid, c_log2);
   }
   // At most four full pages remain: k (in b0) and k + 1 (in b1) are already issued.
   const int rem = n_full - k;
@@ -389,12 +431,12 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <bool kOutBf16>
+template <bool kOutBf16, bool kFused>
 __global__ __launch_bounds__(64) void merge_partitions_kernel(DecodeParams p) {
   const int b = blockIdx.x / p.num_q_heads;
   const int h = blockIdx.x % p.num_q_heads;
   const int lane = threadIdx.x;
-  const int L = p.context_lens[b];
+  const int L = context_length<kFused>(p, b);
   const bool len_ok = L > 0 && L <= p.max_blocks * kBlock;
   const int n_pages = len_ok ? (L + kBlock - 1) / kBlock : 0;
   bool bad = false;
@@ -437,23 +479,28 @@ __global__ __launch_bounds__(64) void merge_partitions_kernel(DecodeParams p) {
 
 }  // namespace
 
-hipError_t launch_paged_decode(const DecodeParams &p, bool out_bf16, hipStream_t stream) {
+template <bool kFused>
+hipError_t launch_variant(const DecodeParams &p, bool out_bf16, hipStream_t stream) {
   const int64_t groups = (int64_t)p.batch * p.num_kv_heads * p.num_parts;
   if (groups == 0) return hipSuccess;
   if (groups > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)groups), block(kThreads);
   if (p.num_parts == 1) {
-    if (out_bf16) hipLaunchKernelGGL((paged_decode_kernel<false, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((paged_decode_kernel<false, false>), grid, block, 0, stream, p);
+    if (out_bf16) hipLaunchKernelGGL((paged_decode_kernel<false, true, kFused>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((paged_decode_kernel<false, false, kFused>), grid, block, 0, stream, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((paged_decode_kernel<true, true>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((paged_decode_kernel<true, true, kFused>), grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 mgrid((unsigned)((int64_t)p.batch * p.num_q_heads));
-  if (out_bf16) hipLaunchKernelGGL((merge_partitions_kernel<true>), mgrid, dim3(64), 0, stream, p);
-  else hipLaunchKernelGGL((merge_partitions_kernel<false>), mgrid, dim3(64), 0, stream, p);
+  if (out_bf16) hipLaunchKernelGGL((merge_partitions_kernel<true, kFused>), mgrid, dim3(64), 0, stream, p);
+  else hipLaunchKernelGGL((merge_partitions_kernel<false, kFused>), mgrid, dim3(64), 0, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_paged_decode(const DecodeParams &p, bool out_bf16, hipStream_t stream) {
+  return p.positions ? launch_variant<true>(p, out_bf16, stream) : launch_variant<false>(p, out_bf16, stream);
 }
 
 }  // namespace pkv

@@ -183,13 +183,17 @@ extern "C" pkv_status pkv_rope_kv_append(const pkv_pool *pool, const int32_t *bl
   return pkv::launch_rope_append(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-extern "C" pkv_status pkv_paged_decode_attention(const void *q, const void *k_pool, const void *v_pool,
-                                                 int32_t num_pages, const int32_t *block_tables,
-                                                 int32_t max_blocks_per_seq, const int32_t *context_lens, void *out,
-                                                 pkv_out_dtype out_dtype, int32_t batch, int32_t num_q_heads,
-                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                                 float scale, int32_t partition_pages, void *workspace,
-                                                 size_t workspace_bytes, void *stream) {
+namespace {
+
+// Shared by the attention call and the fused decode step.  `positions` != nullptr selects the
+// fused step: the context is positions[b] + 1 and k_new / v_new are appended on the way.
+pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, int32_t num_pages,
+                         const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                         const int32_t *positions, const void *k_new, const void *v_new, void *out,
+                         pkv_out_dtype out_dtype, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, float scale, int32_t partition_pages, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  const bool fused = positions != nullptr;
   if (batch < 0 || num_pages <= 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0)
     return PKV_ERR_SHAPE;
   if (!(scale > 0.0f) || !isfinite(scale)) return PKV_ERR_SHAPE;
@@ -197,8 +201,10 @@ extern "C" pkv_status pkv_paged_decode_attention(const void *q, const void *k_po
   if (head_dim != pkv::kHeadDim || block_size != pkv::kBlock || num_q_heads != pkv::kGroup * num_kv_heads)
     return PKV_ERR_UNSUPPORTED;
   if (batch == 0) return PKV_OK;
-  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (!q || !k_pool || !v_pool || !block_tables || !out) return PKV_ERR_NULL;
+  if (fused ? (!k_new || !v_new) : !context_lens) return PKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PKV_ERR_ALIGNMENT;
+  if (fused && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGNMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   int32_t part_pages = partition_pages;
@@ -218,9 +224,13 @@ extern "C" pkv_status pkv_paged_decode_attention(const void *q, const void *k_po
   if (debug_validate_enabled()) {
     std::vector<int32_t> bt, lens;
     pkv_status st = copy_to_host(bt, block_tables, (size_t)batch * max_blocks_per_seq, s);
-    if (st == PKV_OK) st = copy_to_host(lens, context_lens, (size_t)batch, s);
+    if (st == PKV_OK) st = copy_to_host(lens, fused ? positions : context_lens, (size_t)batch, s);
     if (st != PKV_OK) return st;
-    st = pkv_validate_decode_host(bt.data(), max_blocks_per_seq, lens.data(), batch, num_pages, nullptr);
+    if (fused) {
+      st = pkv_validate_append_host(bt.data(), max_blocks_per_seq, lens.data(), batch, num_pages, nullptr);
+      for (auto &l : lens) l += 1;  // the context after the append
+    }
+    if (st == PKV_OK) st = pkv_validate_decode_host(bt.data(), max_blocks_per_seq, lens.data(), batch, num_pages, nullptr);
     if (st != PKV_OK) return st;
   }
 
@@ -246,5 +256,36 @@ extern "C" pkv_status pkv_paged_decode_attention(const void *q, const void *k_po
   p.part_pages = part_pages;
   p.num_parts = num_parts;
   p.score_log2 = scale * 1.4426950408889634f;
+  p.positions = positions;
+  p.k_new = static_cast<const uint16_t *>(k_new);
+  p.v_new = static_cast<const uint16_t *>(v_new);
+  p.k_pool_w = fused ? const_cast<uint16_t *>(p.k_pool) : nullptr;
+  p.v_pool_w = fused ? const_cast<uint16_t *>(p.v_pool) : nullptr;
   return pkv::launch_paged_decode(p, out_dtype == PKV_OUT_BF16, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_decode_attention(const void *q, const void *k_pool, const void *v_pool,
+                                                 int32_t num_pages, const int32_t *block_tables,
+                                                 int32_t max_blocks_per_seq, const int32_t *context_lens, void *out,
+                                                 pkv_out_dtype out_dtype, int32_t batch, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                 float scale, int32_t partition_pages, void *workspace,
+                                                 size_t workspace_bytes, void *stream) {
+  return decode_common(q, k_pool, v_pool, num_pages, block_tables, max_blocks_per_seq, context_lens, nullptr, nullptr,
+                       nullptr, out, out_dtype, batch, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                       partition_pages, workspace, workspace_bytes, stream);
+}
+
+extern "C" pkv_status pkv_decode_step(const pkv_pool *pool, const void *q, const int32_t *block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t *positions, const void *k_new,
+                                      const void *v_new, void *out, pkv_out_dtype out_dtype, int32_t batch,
+                                      int32_t num_q_heads, float scale, int32_t partition_pages, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  if (!pool) return PKV_ERR_NULL;
+  if (batch > 0 && !positions) return PKV_ERR_NULL;
+  return decode_common(q, pool->k_pool, pool->v_pool, pool->num_pages, block_tables, max_blocks_per_seq, nullptr,
+                       positions, k_new, v_new, out, out_dtype, batch, num_q_heads, pool->num_kv_heads, pool->head_dim,
+                       pool->block_size, scale, partition_pages, workspace, workspace_bytes, stream);
 }

@@ -45,6 +45,13 @@ struct DecodeParams {
   int32_t part_pages;  // pages per partition
   int32_t num_parts;   // ceil(max_blocks / part_pages)
   float score_log2;    // scale * log2(e): scores are kept in log2 units so exp2 does the softmax
+  // Fused decode step (positions != nullptr): the context is positions[b] + 1 and the new rows
+  // k_new / v_new are written at that position by the workgroup that reads the last page.
+  const int32_t *positions;
+  const uint16_t *k_new;  // [batch][num_kv_heads][kHeadDim]
+  const uint16_t *v_new;
+  uint16_t *k_pool_w;     // the same pools, writable
+  uint16_t *v_pool_w;
 };
 
 struct RopeAppendParams {

@@ -129,6 +129,24 @@ def test_rope_append_host_checks(lib):
     assert call(q=FAKE + 2) == ALIGN
 
 
+def test_decode_step_host_checks(lib):
+    good = pkv.Pool(FAKE, FAKE, 8, 8, 64, 16)
+
+    def call(pool=ctypes.byref(good), q=FAKE, pos=FAKE, kn=FAKE, out=FAKE, batch=1, hq=32, scale=0.125, pp=128, ws=None,
+             wsb=0):
+        return lib.pkv_decode_step(pool, q, FAKE, 128, pos, kn, FAKE, out, 0, batch, hq, scale, pp, ws, wsb, None)
+
+    assert call(pool=None) == NULL
+    assert call(pos=None) == NULL
+    assert call(kn=None) == NULL
+    assert call(batch=-1) == SHAPE
+    assert call(scale=-1.0) == SHAPE
+    assert call(hq=8) == UNSUP
+    assert call(batch=0) == OK
+    assert call(kn=FAKE + 2) == ALIGN
+    assert call(pp=4) == WS
+
+
 def test_host_validators():
     bt = np.full((3, 4), -1, dtype=np.int32)
     bt[0, :2] = [5, 6]
