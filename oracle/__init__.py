@@ -18,3 +18,4 @@ from .paged_oracle import (  # noqa: F401
     softmax_two_pass,
 )
 from .rope_oracle import bf16_bits_to_f32, rope_kv_append, rope_pair_index, rope_rotate  # noqa: F401,E402
+from .allocator_oracle import AllocatorModel  # noqa: F401,E402
