@@ -4,8 +4,10 @@
  *
  * Two calls carry the method: pkv_kv_append writes each sequence's new K/V row into its page,
  * and pkv_paged_decode_attention streams each sequence's pages with grouped-query attention and
- * an FP32 online softmax.  The rest are helpers (planning, workspace size, host-side
- * validation, status strings).
+ * an FP32 online softmax.  pkv_rope_kv_append and pkv_decode_step fuse the rotary embedding
+ * into the append and the append into the attention launch.  The pkv_alloc_* calls are the
+ * host page allocator that fills the block tables.  The rest are helpers (planning, workspace
+ * size, host-side validation, status strings).
  *
  * Conventions for every call:
  *   - Pointers documented as "device" must point to GPU memory of the current HIP device;
@@ -57,7 +59,10 @@ typedef enum {
   PKV_ERR_WORKSPACE = 4,   /* the chosen split needs more workspace than was passed         */
   PKV_ERR_VALIDATION = 5,  /* debug validation rejected the data (PKV_DEBUG_VALIDATE=1)     */
   PKV_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed                    */
-  PKV_ERR_ALIGNMENT = 7    /* a device buffer is not 16-byte aligned                        */
+  PKV_ERR_ALIGNMENT = 7,   /* a device buffer is not 16-byte aligned                        */
+  PKV_ERR_REJECTED = 8,    /* allocator: the request can never be served (see pkv_alloc_*)  */
+  PKV_ERR_STATE = 9,       /* allocator: unknown request id, or an id already queued/active */
+  PKV_ERR_EXHAUSTED = 10   /* allocator: the page would exceed the request's credits        */
 } pkv_status;
 
 typedef enum {
@@ -223,6 +228,82 @@ pkv_status pkv_validate_append_host(const int32_t *block_tables, int32_t max_blo
                                     int32_t batch, int32_t num_pages, int32_t *bad_row);
 pkv_status pkv_validate_decode_host(const int32_t *block_tables, int32_t max_blocks_per_seq,
                                     const int32_t *context_lens, int32_t batch, int32_t num_pages, int32_t *bad_row);
+
+/*
+ * Host page allocator with admission credits (plain C++, no GPU; step a0 of a decode loop:
+ * it produces the block tables the calls above read).
+ *
+ * Rules ("6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference", section
+ * "Current scope"; "The prefill path: flowing the entire prompt at once", section
+ * "Distributing K/V into paged blocks"):
+ *   - A request of P prompt tokens asking for N new tokens may generate A = min(N, C - P)
+ *     tokens (C = 16 * max_blocks_per_seq, the context limit).  Its last generated token is
+ *     never appended, so the longest prefix it stores is max(P, P + A - 1) tokens, and
+ *     admission reserves that many 16-token pages in every layer as credits.
+ *   - Requests are admitted first-in-first-out while their credits fit beside those of the
+ *     active requests; the first one that does not fit blocks the queue (no skipping, no
+ *     preemption).  Static batching admits only when no request is active.
+ *   - Physical pages are taken lazily, from the back of the free list, the first time a
+ *     position of a block is needed; a table entry of -1 is "unassigned".  A request never
+ *     holds more pages than its credits, so an admitted request always finds its pages.
+ *   - Release returns the request's pages to the back of the free list (layer by layer, each
+ *     in block order) and its credits to the pool.
+ *
+ * The allocator is a host object owned by the caller (create/destroy); it is not thread-safe
+ * (one caller thread at a time).  All pointers are host pointers.
+ */
+typedef struct pkv_allocator pkv_allocator;
+
+typedef struct {
+  int64_t pool_pages;       /* pages in the pool                                          */
+  int64_t free_pages;       /* pages on the free list now                                 */
+  int64_t credits_reserved; /* credits held by active requests                            */
+  int64_t active;           /* admitted, not yet released                                 */
+  int64_t waiting;          /* queued, not yet admitted                                   */
+  int64_t peak_active;      /* most requests active at once (checked after each admit)    */
+  int64_t peak_assigned;    /* most pages assigned at once                                */
+  int64_t largest_batch;    /* largest batch passed to pkv_alloc_prepare_step             */
+  int64_t admission_waits;  /* admission passes that stopped at a request that did not fit */
+  int64_t rejected;         /* submissions refused with PKV_ERR_REJECTED                  */
+} pkv_alloc_stats;
+
+/* Create an allocator over num_pages pages shared by `layers` layers, each request's table
+ * holding max_blocks_per_seq entries per layer.  free_order (NULL = 0, 1, ..., num_pages - 1)
+ * is the initial free list, a permutation of [0, num_pages); pages are taken from its end.
+ * PKV_ERR_SHAPE for non-positive sizes or a free_order that is not a permutation. */
+pkv_status pkv_alloc_create(int32_t num_pages, int32_t layers, int32_t max_blocks_per_seq, const int32_t *free_order,
+                            int32_t static_batching, pkv_allocator **out);
+void pkv_alloc_destroy(pkv_allocator *alloc);
+
+/* Queue a request.  PKV_ERR_REJECTED (counted in `rejected`) when prompt_tokens is outside
+ * [1, C], max_new_tokens < 0, or its credits exceed the whole pool; PKV_ERR_STATE when the id
+ * is already queued or active. */
+pkv_status pkv_alloc_submit(pkv_allocator *alloc, int64_t request_id, int32_t prompt_tokens, int32_t max_new_tokens);
+
+/* One admission pass: admit queued requests in order while their credits fit (at most
+ * `capacity` of them), writing their ids to admitted[0 .. *count). */
+pkv_status pkv_alloc_admit(pkv_allocator *alloc, int64_t *admitted, int32_t capacity, int32_t *count);
+
+/* Make the page holding token `pos` present in every layer of an active request.
+ * PKV_ERR_STATE for an unknown id, PKV_ERR_SHAPE for pos outside [0, C), PKV_ERR_EXHAUSTED
+ * when it would exceed the request's credits (nothing is assigned then). */
+pkv_status pkv_alloc_ensure(pkv_allocator *alloc, int64_t request_id, int32_t pos);
+
+/* Decode-step tables: for b = 0 .. batch-1 in order, pkv_alloc_ensure(ids[b], positions[b]);
+ * then write the block tables of all rows to block_tables, int32[layers][batch][max_blocks],
+ * the layout pkv_kv_append / pkv_paged_decode_attention read per layer.  On the first failure
+ * *bad_row gets its row, pages ensured for earlier rows stay assigned and nothing is written;
+ * on success *bad_row = -1 and `largest_batch` is updated. */
+pkv_status pkv_alloc_prepare_step(pkv_allocator *alloc, const int64_t *request_ids, const int32_t *positions,
+                                  int32_t batch, int32_t *block_tables, int32_t *bad_row);
+
+/* Copy an active request's table, int32[layers][max_blocks], to dst. */
+pkv_status pkv_alloc_table(const pkv_allocator *alloc, int64_t request_id, int32_t *dst);
+
+/* Finish a request: return its pages and credits.  PKV_ERR_STATE for an unknown id. */
+pkv_status pkv_alloc_release(pkv_allocator *alloc, int64_t request_id);
+
+pkv_status pkv_alloc_get_stats(const pkv_allocator *alloc, pkv_alloc_stats *out);
 
 #ifdef __cplusplus
 }

@@ -15,13 +15,17 @@ K/V into paged blocks":
   waiting request blocks the ones behind it.  A request whose budget exceeds the whole pool is
   rejected.
 * Completion returns the request's pages (to the back of the free list) and its remaining credits.
+* Static batching admits the next group only once every active request has finished; continuous
+  batching admits whenever credits allow.
 * A request never holds more physical pages than its credits, so with the sum of credits of the
   active requests within the pool, no lazy assignment of an admitted request can fail.
 
 Readings where the page is silent: the allowed output is ``min(max_new, context - prompt)`` (prompt
 plus output fit in the context); a request processes at least its prompt, so the prefix is
 ``max(prompt, prompt + allowed_new - 1)``; "admission waits" counts admission passes that stopped
-at a request that did not fit.
+at a request that did not fit; released pages go back layer by layer in block order; a request id
+may not be queued twice; one admission pass may be capped at ``limit`` requests (a cap is not a
+wait).
 """
 
 from __future__ import annotations
@@ -46,7 +50,8 @@ class Request:
 
 
 class AllocatorModel:
-    def __init__(self, num_pages: int, layers: int, max_blocks: int, free_order=None):
+    def __init__(self, num_pages: int, layers: int, max_blocks: int, free_order=None, static: bool = False):
+        self.static = static
         self.num_pages = num_pages
         self.layers = layers
         self.max_blocks = max_blocks
@@ -66,6 +71,8 @@ class AllocatorModel:
 
     def submit(self, rid: int, prompt: int, max_new: int) -> bool:
         """Queue a request; False (and counted as rejected) when it can never fit."""
+        if rid in self.active or any(r.rid == rid for r in self.waiting):
+            return False  # duplicate id: refused, not counted
         if prompt <= 0 or prompt > self.context or max_new < 0:
             self.stats["rejected"] += 1
             return False
@@ -76,15 +83,20 @@ class AllocatorModel:
         self.waiting.append(Request(rid, prompt, max_new, credits=need))
         return True
 
-    def admit(self) -> list[int]:
+    def admit(self, limit: int | None = None) -> list[int]:
         admitted = []
-        while self.waiting and self.credits_reserved + self.waiting[0].credits <= self.num_pages:
+        if self.static and self.active:
+            if self.waiting:
+                self.stats["admission_waits"] += 1
+            return admitted
+        while self.waiting and (limit is None or len(admitted) < limit) \
+                and self.credits_reserved + self.waiting[0].credits <= self.num_pages:
             r = self.waiting.pop(0)
             r.tables = [[-1] * self.max_blocks for _ in range(self.layers)]
             self.active[r.rid] = r
             self.credits_reserved += r.credits
             admitted.append(r.rid)
-        if self.waiting:
+        if self.waiting and (limit is None or len(admitted) < limit):
             self.stats["admission_waits"] += 1
         self.stats["peak_active"] = max(self.stats["peak_active"], len(self.active))
         return admitted
@@ -111,6 +123,20 @@ class AllocatorModel:
 
     def note_batch(self, size: int) -> None:
         self.stats["largest_batch"] = max(self.stats["largest_batch"], size)
+
+    def prepare_step(self, rids, positions):
+        """One decode step's tables: ensure each row's page in turn (stopping at the first failure,
+        whose row index is returned) and return int32 tables [layers][batch][max_blocks]."""
+        import numpy as np
+
+        for i, (rid, pos) in enumerate(zip(rids, positions)):
+            if not self.ensure(int(rid), int(pos)):
+                return None, i
+        out = np.full((self.layers, len(rids), self.max_blocks), -1, dtype=np.int32)
+        for i, rid in enumerate(rids):
+            out[:, i, :] = np.asarray(self.active[int(rid)].tables, dtype=np.int32)
+        self.note_batch(len(rids))
+        return out, -1
 
     def table(self, rid: int):
         return [list(row) for row in self.active[rid].tables]

@@ -1,7 +1,8 @@
 """Paged KV cache decode step for AMD Instinct MI355X (gfx950).
 
 ``kv_append`` and ``paged_decode_attention`` are thin bindings of the C ABI in
-``include/pagedkv.h``; the work runs in hand-written HIP kernels (``csrc/``).  PyTorch supplies
+``include/pagedkv.h``; the work runs in hand-written HIP kernels (``csrc/``).  ``PageAllocator``
+binds the host page allocator (C++) that fills the block tables.  PyTorch supplies
 device memory and the current stream only.
 """
 
@@ -9,6 +10,8 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     PKV_OUT_BF16,
     PKV_OUT_F32,
+    AllocStats,
+    PageAllocator,
     SIGNATURES,
     STATUS_NAMES,
     PagedKVError,

@@ -26,6 +26,9 @@ STATUS_NAMES = {
     5: "PKV_ERR_VALIDATION",
     6: "PKV_ERR_HIP",
     7: "PKV_ERR_ALIGNMENT",
+    8: "PKV_ERR_REJECTED",
+    9: "PKV_ERR_STATE",
+    10: "PKV_ERR_EXHAUSTED",
 }
 
 # Every symbol the header declares, with its ctypes signature.
@@ -43,6 +46,12 @@ class Pool(ctypes.Structure):
         ("head_dim", _c_int32),
         ("block_size", _c_int32),
     ]
+
+
+class AllocStats(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "pool_pages", "free_pages", "credits_reserved", "active", "waiting", "peak_active", "peak_assigned",
+        "largest_batch", "admission_waits", "rejected")]
 
 
 SIGNATURES = {
@@ -68,6 +77,15 @@ SIGNATURES = {
     "pkv_device_cu_count": (_c_int32, []),
     "pkv_validate_append_host": (ctypes.c_int, [_vp, _c_int32, _vp, _c_int32, _c_int32, _vp]),
     "pkv_validate_decode_host": (ctypes.c_int, [_vp, _c_int32, _vp, _c_int32, _c_int32, _vp]),
+    "pkv_alloc_create": (ctypes.c_int, [_c_int32, _c_int32, _c_int32, _vp, _c_int32, ctypes.POINTER(_vp)]),
+    "pkv_alloc_destroy": (None, [_vp]),
+    "pkv_alloc_submit": (ctypes.c_int, [_vp, ctypes.c_int64, _c_int32, _c_int32]),
+    "pkv_alloc_admit": (ctypes.c_int, [_vp, _vp, _c_int32, ctypes.POINTER(_c_int32)]),
+    "pkv_alloc_ensure": (ctypes.c_int, [_vp, ctypes.c_int64, _c_int32]),
+    "pkv_alloc_prepare_step": (ctypes.c_int, [_vp, _vp, _vp, _c_int32, _vp, ctypes.POINTER(_c_int32)]),
+    "pkv_alloc_table": (ctypes.c_int, [_vp, ctypes.c_int64, _vp]),
+    "pkv_alloc_release": (ctypes.c_int, [_vp, ctypes.c_int64]),
+    "pkv_alloc_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(AllocStats)]),
 }
 
 _lib = None
@@ -378,3 +396,79 @@ def validate_decode_host(block_tables, context_lens, num_pages: int):
         bt.ctypes.data, bt.shape[1] if bt.ndim == 2 else 0, lens.ctypes.data, lens.shape[0], num_pages, ctypes.byref(bad)
     )
     return int(st), int(bad.value)
+
+
+class PageAllocator:
+    """Host page allocator with admission credits (the ``pkv_alloc_*`` calls of the C ABI).
+
+    Methods return the C status (``submit``, ``ensure``, ``release``) or raise ``PagedKVError``
+    on argument errors; tables come back as numpy int32 arrays."""
+
+    def __init__(self, num_pages: int, layers: int, max_blocks: int, free_order=None, static: bool = False):
+        import numpy as np
+
+        self.layers, self.max_blocks = int(layers), int(max_blocks)
+        self._order = None if free_order is None else np.ascontiguousarray(free_order, dtype=np.int32)
+        if self._order is not None and self._order.shape != (num_pages,):
+            raise ValueError("free_order must hold num_pages entries")
+        handle = _vp()
+        st = library().pkv_alloc_create(num_pages, layers, max_blocks,
+                                        None if self._order is None else self._order.ctypes.data, int(bool(static)),
+                                        ctypes.byref(handle))
+        _check("pkv_alloc_create", st)
+        self._h = handle
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            library().pkv_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def submit(self, request_id: int, prompt_tokens: int, max_new_tokens: int) -> int:
+        return int(library().pkv_alloc_submit(self._h, request_id, prompt_tokens, max_new_tokens))
+
+    def admit(self, capacity: int = 1 << 20) -> list:
+        import numpy as np
+
+        ids = np.zeros(max(capacity, 1), dtype=np.int64)
+        n = ctypes.c_int32(0)
+        _check("pkv_alloc_admit", library().pkv_alloc_admit(self._h, ids.ctypes.data, capacity, ctypes.byref(n)))
+        return [int(x) for x in ids[: n.value]]
+
+    def ensure(self, request_id: int, pos: int) -> int:
+        return int(library().pkv_alloc_ensure(self._h, request_id, pos))
+
+    def prepare_step(self, request_ids, positions, out=None):
+        """(status, bad_row, tables int32[layers][batch][max_blocks])."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+        pos = np.ascontiguousarray(positions, dtype=np.int32)
+        if ids.shape != pos.shape or ids.ndim != 1:
+            raise ValueError("request_ids and positions must be 1-D of one length")
+        shape = (self.layers, ids.shape[0], self.max_blocks)
+        if out is None:
+            out = np.empty(shape, dtype=np.int32)
+        elif out.shape != shape or out.dtype != np.int32 or not out.flags.c_contiguous:
+            raise ValueError(f"out must be a contiguous int32 array of shape {shape}")
+        bad = ctypes.c_int32(-2)
+        st = library().pkv_alloc_prepare_step(self._h, ids.ctypes.data, pos.ctypes.data, ids.shape[0],
+                                              out.ctypes.data, ctypes.byref(bad))
+        return int(st), int(bad.value), out
+
+    def table(self, request_id: int):
+        import numpy as np
+
+        out = np.empty((self.layers, self.max_blocks), dtype=np.int32)
+        _check("pkv_alloc_table", library().pkv_alloc_table(self._h, request_id, out.ctypes.data))
+        return out
+
+    def release(self, request_id: int) -> int:
+        return int(library().pkv_alloc_release(self._h, request_id))
+
+    def stats(self) -> dict:
+        st = AllocStats()
+        _check("pkv_alloc_get_stats", library().pkv_alloc_get_stats(self._h, ctypes.byref(st)))
+        return {name: int(getattr(st, name)) for name, _ in AllocStats._fields_}

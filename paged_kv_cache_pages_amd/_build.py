@@ -21,7 +21,7 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
 
 HIP_SOURCES = ["pagedkv_api.hip", "kv_append.hip", "paged_attention.hip", "rope_append.hip"]
-CXX_SOURCES = ["validate.cpp"]
+CXX_SOURCES = ["validate.cpp", "page_allocator.cpp"]
 
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIP_FLAGS = [

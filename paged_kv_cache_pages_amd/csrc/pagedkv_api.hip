@@ -47,6 +47,9 @@ extern "C" const char *pkv_status_string(pkv_status status) {
     case PKV_ERR_VALIDATION: return "debug validation rejected the block table, positions or context lengths";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_ALIGNMENT: return "a device buffer is not 16-byte aligned";
+    case PKV_ERR_REJECTED: return "request rejected: invalid lengths, or its page credits exceed the whole pool";
+    case PKV_ERR_STATE: return "unknown request id, or the id is already queued or active";
+    case PKV_ERR_EXHAUSTED: return "the page would exceed the request's admission credits";
   }
   return "unknown status";
 }

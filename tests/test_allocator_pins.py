@@ -87,3 +87,43 @@ def test_invariants_under_random_operations(ops):
         assert all(r.assigned <= r.credits for r in m.active.values())
         # every admitted request can still take all of its remaining credits as pages
         assert sum(r.credits - r.assigned for r in m.active.values()) <= len(m.free)
+
+
+def test_static_batching_waits_for_the_whole_group():
+    m = AllocatorModel(num_pages=100, layers=1, max_blocks=128, static=True)
+    for rid in (1, 2, 3):
+        assert m.submit(rid, 16, 1)
+    assert m.admit() == [1, 2, 3]
+    assert m.submit(4, 16, 1)
+    assert m.admit() == [] and m.snapshot()["admission_waits"] == 1
+    m.release(1)
+    m.release(2)
+    assert m.admit() == []  # request 3 still runs
+    m.release(3)
+    assert m.admit() == [4]
+
+
+def test_admission_limit_and_duplicates():
+    m = AllocatorModel(num_pages=100, layers=1, max_blocks=128)
+    for rid in (1, 2, 3):
+        assert m.submit(rid, 16, 1)
+    assert not m.submit(2, 16, 1)  # already queued
+    assert m.admit(limit=2) == [1, 2]
+    assert m.snapshot()["admission_waits"] == 0  # a capped pass is not a wait
+    assert not m.submit(1, 16, 1)  # already active
+    assert m.snapshot()["rejected"] == 0
+    assert m.admit() == [3]
+
+
+def test_prepare_step_tables_and_first_failure():
+    m = AllocatorModel(num_pages=8, layers=2, max_blocks=3, free_order=list(range(8)))
+    assert m.submit(5, 16, 1) and m.submit(6, 17, 1)  # 2 and 4 credits
+    assert m.admit() == [5, 6]
+    tables, bad = m.prepare_step([5, 6], [15, 16])
+    assert bad == -1 and tables.shape == (2, 2, 3)
+    assert tables[:, 0].tolist() == [[7, -1, -1], [6, -1, -1]]
+    assert tables[:, 1].tolist() == [[-1, 5, -1], [-1, 4, -1]]  # only the block holding position 16
+    assert m.snapshot()["largest_batch"] == 2
+    tables, bad = m.prepare_step([6, 5], [0, 16])  # request 5 has no credit for a second page
+    assert tables is None and bad == 1
+    assert m.table(6)[0][:2] == [3, 5]
