@@ -1,0 +1,81 @@
+"""A continuous-batching decode loop on the GPU driven by the C++ page allocator.
+
+Requests are admitted by their page credits, their prompt K/V rows are written with kv_append
+(one row per prompt token), then every decode step takes its block tables from
+pkv_alloc_prepare_step and runs pkv_decode_step per layer.  Finished requests release their
+pages, which later requests reuse while the old K/V rows are still in them.  Every step's
+output is checked against the FP64 oracle run on the same tables, and the pools against the
+oracle's appends, bit for bit.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import assert_close, bf16_to_bits, to_gpu_bf16, to_gpu_i32
+from workloads import normal_bf16
+
+pytestmark = pytest.mark.gpu
+
+HKV, HQ, D = 8, 32, 64
+
+
+@pytest.mark.parametrize("static", [False, True])
+def test_continuous_batching_loop(gpu, static):
+    import torch
+
+    rng = np.random.default_rng(11 + static)
+    layers, max_blocks, num_pages = 2, 16, 2 * 30
+    alloc = gpu.PageAllocator(num_pages, layers, max_blocks, free_order=rng.permutation(num_pages), static=static)
+    k_ref = normal_bf16(rng, (num_pages, HKV, 16, D))  # stale rows the requests never wrote
+    v_ref = normal_bf16(rng, (num_pages, HKV, 16, D))
+    kp, vp = to_gpu_bf16(k_ref), to_gpu_bf16(v_ref)
+    reqs = {rid: (int(rng.integers(1, 140)), int(rng.integers(0, 40))) for rid in range(12)}
+    for rid, (p, n) in reqs.items():
+        assert alloc.submit(rid, p, n) == 0
+    pos, left, done, steps = {}, {}, 0, 0
+    while done < len(reqs):
+        for rid in alloc.admit():
+            p, n = reqs[rid]
+            for t in range(p):
+                assert alloc.ensure(rid, t) == 0
+            table = alloc.table(rid)
+            positions = np.arange(p, dtype=np.int32)
+            for layer in range(layers):
+                bt = np.repeat(table[layer][None, :], p, axis=0)
+                kn, vn = normal_bf16(rng, (p, HKV, D)), normal_bf16(rng, (p, HKV, D))
+                gpu.kv_append(kp, vp, to_gpu_i32(bt), to_gpu_i32(positions), to_gpu_bf16(kn), to_gpu_bf16(vn))
+                k_ref, v_ref = oracle.kv_append(k_ref, v_ref, bt, positions, kn, vn)
+            pos[rid], left[rid] = p, min(n, max_blocks * 16 - p) - 1  # the first output comes from prefill
+        rows = sorted(r for r in pos if left[r] > 0)
+        if rows:
+            st, bad, tables = alloc.prepare_step(rows, [pos[r] for r in rows])
+            assert st == 0, (st, bad)
+            positions = np.array([pos[r] for r in rows], dtype=np.int32)
+            print(f"[loop static={static}] step {steps} batch {len(rows)} max_pos {positions.max()}", flush=True)
+            pp = 4 if steps % 2 else 0  # alternate a forced 4-page split with the planned one
+            for layer in range(layers):
+                q = normal_bf16(rng, (len(rows), HQ, D))
+                kn, vn = normal_bf16(rng, (len(rows), HKV, D)), normal_bf16(rng, (len(rows), HKV, D))
+                out = gpu.decode_step(to_gpu_bf16(q), kp, vp, to_gpu_i32(tables[layer]), to_gpu_i32(positions),
+                                      to_gpu_bf16(kn), to_gpu_bf16(vn), out_dtype=torch.float32, partition_pages=pp)
+                k_ref, v_ref = oracle.kv_append(k_ref, v_ref, tables[layer], positions, kn, vn)
+                ref = oracle.paged_decode_attention(q, k_ref, v_ref, tables[layer], positions + 1)
+                torch.cuda.synchronize()
+                assert_close(out.cpu().numpy(), ref, f"step {steps} layer {layer}")
+            steps += 1
+        for r in list(pos):
+            if left[r] > 0:
+                pos[r] += 1
+                left[r] -= 1
+            if left[r] <= 0:
+                assert alloc.release(r) == 0
+                del pos[r], left[r]
+                done += 1
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_bits(kp), k_ref) and np.array_equal(bf16_to_bits(vp), v_ref)
+    s = alloc.stats()
+    assert s["free_pages"] == num_pages and s["active"] == 0
+    assert s["largest_batch"] >= 2 and steps > 20
+    if not static:
+        assert s["admission_waits"] > 0  # the pool is small enough that requests queue
