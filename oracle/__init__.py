@@ -19,3 +19,4 @@ from .paged_oracle import (  # noqa: F401
 )
 from .rope_oracle import bf16_bits_to_f32, rope_kv_append, rope_pair_index, rope_rotate  # noqa: F401,E402
 from .allocator_oracle import AllocatorModel  # noqa: F401,E402
+from .prefill_oracle import causal_attention_rows, paged_prefill_attention, prefill_kv_append  # noqa: F401,E402

@@ -29,3 +29,4 @@ from .configs import (  # noqa: F401
     make_custom,
     normal_bf16,
 )
+from .prefill import PREFILL_CONFIGS, PrefillWorkload, make_prefill, make_prefill_config  # noqa: F401,E402
