@@ -5,9 +5,10 @@
  * Two calls carry the method: pkv_kv_append writes each sequence's new K/V row into its page,
  * and pkv_paged_decode_attention streams each sequence's pages with grouped-query attention and
  * an FP32 online softmax.  pkv_rope_kv_append and pkv_decode_step fuse the rotary embedding
- * into the append and the append into the attention launch.  The pkv_alloc_* calls are the
- * host page allocator that fills the block tables.  The rest are helpers (planning, workspace
- * size, host-side validation, status strings).
+ * into the append and the append into the attention launch.  pkv_prefill_kv_append and
+ * pkv_paged_prefill_attention are the prompt-side pair (many rows per sequence, causal).  The
+ * pkv_alloc_* calls are the host page allocator that fills the block tables.  The rest are
+ * helpers (planning, workspace size, host-side validation, status strings).
  *
  * Conventions for every call:
  *   - Pointers documented as "device" must point to GPU memory of the current HIP device;
@@ -228,6 +229,58 @@ pkv_status pkv_validate_append_host(const int32_t *block_tables, int32_t max_blo
                                     int32_t batch, int32_t num_pages, int32_t *bad_row);
 pkv_status pkv_validate_decode_host(const int32_t *block_tables, int32_t max_blocks_per_seq,
                                     const int32_t *context_lens, int32_t batch, int32_t num_pages, int32_t *bad_row);
+
+/*
+ * Paged prefill ("The prefill path: flowing the entire prompt at once", sections "Distributing
+ * K/V into paged blocks", "Per-head attention scores and GQA", "causalMask and online softmax").
+ *
+ * A prefill step covers `batch` sequences packed into num_tokens rows: sequence b owns rows
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 (device int32[batch+1]) of q, k_new, v_new and out, and its
+ * prompt token i sits at absolute position start_pos[b] + i (device int32[batch]; 0 = a whole
+ * prompt, > 0 = a prompt chunk behind that many tokens already in the cache).  max_prompt_len is a
+ * host-side bound on every cu_seqlens[b+1] - cu_seqlens[b]; it sizes the grids.
+ *
+ * A sequence whose rows are not inside [0, num_tokens), whose length is negative or above
+ * max_prompt_len, is left untouched by both calls.
+ *
+ * pkv_prefill_kv_append writes row i's K and V (device bf16[num_tokens][num_kv_heads][64]) into
+ * slot (start + i) % 16 of page table[(start + i) / 16]; a row whose position is outside the table
+ * or whose entry is outside [0, num_pages) is skipped.  Rows of one call must target distinct
+ * (page, slot) pairs.
+ *
+ * pkv_paged_prefill_attention computes, for every row and query head h, the causal attention of
+ * q (device bf16[num_tokens][num_q_heads][64]) over positions 0 .. start + i of the sequence read
+ * through its block table (KV head h / 4, scale, FP32 online softmax, BF16 products on the matrix
+ * cores), written to out (device, FP32 or BF16 [num_tokens][num_q_heads][64]).  The prompt's own
+ * rows must already be in the pool (call the append first, on the same stream).  When start < 0,
+ * start + length > 16 * max_blocks_per_seq or any of the sequence's first
+ * ceil((start + length) / 16) entries is outside [0, num_pages), all its rows get zeros.  Slots
+ * past the last prompt position are never read.  The prompt's own K/V rows must be finite: a
+ * NaN in row i can reach earlier rows of the same 32-key step through a zero weight.
+ *
+ * Both calls: NULL, shape (negative sizes, num_tokens < 0, max_prompt_len < 0, bad scale or
+ * dtype), unsupported geometry and alignment are reported before launching; nothing is launched
+ * when batch, num_tokens or max_prompt_len is 0.  PKV_DEBUG_VALIDATE=1 also runs
+ * pkv_validate_prefill_host on copies of the tables, cu_seqlens and start_pos.
+ */
+pkv_status pkv_prefill_kv_append(const pkv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t *cu_seqlens, const int32_t *start_pos, const void *k_new,
+                                 const void *v_new, int32_t batch, int32_t num_tokens, int32_t max_prompt_len,
+                                 void *stream);
+pkv_status pkv_paged_prefill_attention(const pkv_pool *pool, const void *q, const int32_t *block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t *cu_seqlens,
+                                       const int32_t *start_pos, void *out, pkv_out_dtype out_dtype, int32_t batch,
+                                       int32_t num_tokens, int32_t max_prompt_len, int32_t num_q_heads, float scale,
+                                       void *stream);
+
+/* Host-side prefill validation (host pointers): cu_seqlens non-decreasing from >= 0 up to
+ * <= num_tokens, every length <= max_prompt_len, start_pos >= 0, start + length within the table,
+ * the first ceil((start + length) / 16) entries in [0, num_pages), and all appended (page, slot)
+ * targets distinct.  *bad_row receives the offending sequence (or -1). */
+pkv_status pkv_validate_prefill_host(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t *cu_seqlens, const int32_t *start_pos, int32_t batch,
+                                     int32_t num_tokens, int32_t max_prompt_len, int32_t num_pages,
+                                     int32_t *bad_row);
 
 /*
  * Host page allocator with admission credits (plain C++, no GPU; step a0 of a decode loop:

@@ -22,9 +22,12 @@ from ._binding import (  # noqa: F401
     kv_append,
     library,
     paged_decode_attention,
+    paged_prefill_attention,
     plan_partition_pages,
+    prefill_kv_append,
     require_library,
     rope_kv_append,
     validate_append_host,
     validate_decode_host,
+    validate_prefill_host,
 )

@@ -77,6 +77,17 @@ SIGNATURES = {
     "pkv_device_cu_count": (_c_int32, []),
     "pkv_validate_append_host": (ctypes.c_int, [_vp, _c_int32, _vp, _c_int32, _c_int32, _vp]),
     "pkv_validate_decode_host": (ctypes.c_int, [_vp, _c_int32, _vp, _c_int32, _c_int32, _vp]),
+    "pkv_prefill_kv_append": (
+        ctypes.c_int,
+        [ctypes.POINTER(Pool), _vp, _c_int32, _vp, _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _vp],
+    ),
+    "pkv_paged_prefill_attention": (
+        ctypes.c_int,
+        [ctypes.POINTER(Pool), _vp, _vp, _c_int32, _vp, _vp, _vp, ctypes.c_int, _c_int32, _c_int32, _c_int32,
+         _c_int32, ctypes.c_float, _vp],
+    ),
+    "pkv_validate_prefill_host": (
+        ctypes.c_int, [_vp, _c_int32, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _vp]),
     "pkv_alloc_create": (ctypes.c_int, [_c_int32, _c_int32, _c_int32, _vp, _c_int32, ctypes.POINTER(_vp)]),
     "pkv_alloc_destroy": (None, [_vp]),
     "pkv_alloc_submit": (ctypes.c_int, [_vp, ctypes.c_int64, _c_int32, _c_int32]),
@@ -370,6 +381,85 @@ def decode_step(q, k_pool, v_pool, block_tables, positions, k_new, v_new, out=No
     )
     _check("pkv_decode_step", st)
     return out
+
+
+def _prefill_args(k_pool, v_pool, block_tables, cu_seqlens, start_pos, max_prompt_len):
+    torch = _torch()
+    _dev_tensor("k_pool", k_pool, torch.bfloat16, 4)
+    _dev_tensor("v_pool", v_pool, torch.bfloat16, 4)
+    _dev_tensor("block_tables", block_tables, torch.int32, 2)
+    _dev_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    _dev_tensor("start_pos", start_pos, torch.int32, 1)
+    if tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_pool and v_pool shapes differ")
+    batch = start_pos.shape[0]
+    if cu_seqlens.shape[0] != batch + 1 or block_tables.shape[0] != batch:
+        raise ValueError("cu_seqlens must hold batch + 1 entries and block_tables batch rows")
+    if max_prompt_len is None:  # convenience only: reads the lengths back to the host
+        max_prompt_len = int(torch.diff(cu_seqlens).max().item()) if batch else 0
+    num_pages, hkv, block, dim = k_pool.shape
+    pool = Pool(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, hkv, dim, block)
+    return pool, batch, int(max_prompt_len)
+
+
+def prefill_kv_append(k_pool, v_pool, block_tables, cu_seqlens, start_pos, k_new, v_new, *, max_prompt_len=None,
+                      stream=None) -> None:
+    """Write the packed prompt rows k_new/v_new [N][Hkv][D] of every sequence at positions
+    start_pos[b] + i through its block table.  ``max_prompt_len`` (a bound on every prompt
+    length) is read back from ``cu_seqlens`` when omitted."""
+    torch = _torch()
+    pool, batch, mpl = _prefill_args(k_pool, v_pool, block_tables, cu_seqlens, start_pos, max_prompt_len)
+    _dev_tensor("k_new", k_new, torch.bfloat16, 3)
+    _dev_tensor("v_new", v_new, torch.bfloat16, 3)
+    if k_new.shape != v_new.shape or k_new.shape[1:] != k_pool.shape[1:2] + k_pool.shape[3:]:
+        raise ValueError("k_new / v_new must be [N][num_kv_heads][head_dim]")
+    st = library().pkv_prefill_kv_append(
+        ctypes.byref(pool), block_tables.data_ptr(), block_tables.shape[1], cu_seqlens.data_ptr(),
+        start_pos.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), batch, k_new.shape[0], mpl,
+        _stream_handle(stream, k_pool.device),
+    )
+    _check("pkv_prefill_kv_append", st)
+
+
+def paged_prefill_attention(q, k_pool, v_pool, block_tables, cu_seqlens, start_pos, out=None, *, max_prompt_len=None,
+                            out_dtype=None, scale=None, stream=None):
+    """Causal attention of the packed prompt rows q [N][Hq][D] over their sequences' pages
+    (positions 0 .. start + i for row i); returns out [N][Hq][D] (bfloat16 by default)."""
+    torch = _torch()
+    pool, batch, mpl = _prefill_args(k_pool, v_pool, block_tables, cu_seqlens, start_pos, max_prompt_len)
+    _dev_tensor("q", q, torch.bfloat16, 3)
+    tokens, hq, dim = q.shape
+    if out is None:
+        out = torch.empty((tokens, hq, dim), dtype=out_dtype or torch.bfloat16, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _dev_tensor("out", out, out.dtype, 3)
+    if tuple(out.shape) != (tokens, hq, dim):
+        raise ValueError("out shape differs from q")
+    if scale is None:
+        scale = 1.0 / float(dim) ** 0.5
+    st = library().pkv_paged_prefill_attention(
+        ctypes.byref(pool), q.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], cu_seqlens.data_ptr(),
+        start_pos.data_ptr(), out.data_ptr(), PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32, batch,
+        tokens, mpl, hq, float(scale), _stream_handle(stream, q.device),
+    )
+    _check("pkv_paged_prefill_attention", st)
+    return out
+
+
+def validate_prefill_host(block_tables, cu_seqlens, start_pos, num_tokens: int, max_prompt_len: int, num_pages: int):
+    """Host-side prefill validation on numpy int32 arrays: (status, bad_sequence)."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    sp = np.ascontiguousarray(start_pos, dtype=np.int32)
+    bad = ctypes.c_int32(-2)
+    st = library().pkv_validate_prefill_host(
+        bt.ctypes.data, bt.shape[1] if bt.ndim == 2 else 0, cu.ctypes.data, sp.ctypes.data, sp.shape[0], num_tokens,
+        max_prompt_len, num_pages, ctypes.byref(bad),
+    )
+    return int(st), int(bad.value)
 
 
 def validate_append_host(block_tables, positions, num_pages: int):

@@ -20,7 +20,7 @@ OBJ_DIR = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
 
-HIP_SOURCES = ["pagedkv_api.hip", "kv_append.hip", "paged_attention.hip", "rope_append.hip"]
+HIP_SOURCES = ["pagedkv_api.hip", "kv_append.hip", "paged_attention.hip", "rope_append.hip", "prefill.hip"]
 CXX_SOURCES = ["validate.cpp", "page_allocator.cpp"]
 
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")

@@ -292,3 +292,95 @@ extern "C" pkv_status pkv_decode_step(const pkv_pool *pool, const void *q, const
                        positions, k_new, v_new, out, out_dtype, batch, num_q_heads, pool->num_kv_heads, pool->head_dim,
                        pool->block_size, scale, partition_pages, workspace, workspace_bytes, stream);
 }
+
+namespace {
+
+pkv_status prefill_checks(const pkv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                          const int32_t *cu_seqlens, const int32_t *start_pos, int32_t batch, int32_t num_tokens,
+                          int32_t max_prompt_len, hipStream_t s) {
+  if (!pool) return PKV_ERR_NULL;
+  if (batch < 0 || num_tokens < 0 || max_prompt_len < 0 || max_blocks_per_seq <= 0 || pool->num_pages <= 0 ||
+      pool->num_kv_heads <= 0)
+    return PKV_ERR_SHAPE;
+  if (pool->head_dim != pkv::kHeadDim || pool->block_size != pkv::kBlock) return PKV_ERR_UNSUPPORTED;
+  if (batch > 65535 || max_prompt_len > 16 * 65535) return PKV_ERR_SHAPE;  // grid y / z limits
+  if (batch == 0 || num_tokens == 0 || max_prompt_len == 0) return PKV_OK;
+  if (!pool->k_pool || !pool->v_pool || !block_tables || !cu_seqlens || !start_pos) return PKV_ERR_NULL;
+  if (!aligned16(pool->k_pool) || !aligned16(pool->v_pool)) return PKV_ERR_ALIGNMENT;
+  if (debug_validate_enabled()) {
+    std::vector<int32_t> bt, cu, st;
+    pkv_status r = copy_to_host(bt, block_tables, (size_t)batch * max_blocks_per_seq, s);
+    if (r == PKV_OK) r = copy_to_host(cu, cu_seqlens, (size_t)batch + 1, s);
+    if (r == PKV_OK) r = copy_to_host(st, start_pos, (size_t)batch, s);
+    if (r != PKV_OK) return r;
+    r = pkv_validate_prefill_host(bt.data(), max_blocks_per_seq, cu.data(), st.data(), batch, num_tokens,
+                                  max_prompt_len, pool->num_pages, nullptr);
+    if (r != PKV_OK) return r;
+  }
+  return PKV_OK;
+}
+
+pkv::PrefillParams prefill_params(const pkv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *cu_seqlens, const int32_t *start_pos, int32_t batch,
+                                  int32_t num_tokens, int32_t max_prompt_len) {
+  pkv::PrefillParams p{};
+  p.k_pool = static_cast<uint16_t *>(pool->k_pool);
+  p.v_pool = static_cast<uint16_t *>(pool->v_pool);
+  p.block_tables = block_tables;
+  p.cu_seqlens = cu_seqlens;
+  p.start_pos = start_pos;
+  p.num_pages = pool->num_pages;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.max_blocks = max_blocks_per_seq;
+  p.batch = batch;
+  p.num_tokens = num_tokens;
+  p.max_prompt_len = max_prompt_len;
+  return p;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_prefill_kv_append(const pkv_pool *pool, const int32_t *block_tables,
+                                            int32_t max_blocks_per_seq, const int32_t *cu_seqlens,
+                                            const int32_t *start_pos, const void *k_new, const void *v_new,
+                                            int32_t batch, int32_t num_tokens, int32_t max_prompt_len, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pool && batch > 0 && num_tokens > 0 && max_prompt_len > 0) {
+    if (!k_new || !v_new) return PKV_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_ALIGNMENT;
+  }
+  pkv_status st = prefill_checks(pool, block_tables, max_blocks_per_seq, cu_seqlens, start_pos, batch, num_tokens,
+                                 max_prompt_len, s);
+  if (st != PKV_OK || batch == 0 || num_tokens == 0 || max_prompt_len == 0) return st;
+  pkv::PrefillParams p =
+      prefill_params(pool, block_tables, max_blocks_per_seq, cu_seqlens, start_pos, batch, num_tokens, max_prompt_len);
+  p.k_new = static_cast<const uint16_t *>(k_new);
+  p.v_new = static_cast<const uint16_t *>(v_new);
+  return pkv::launch_prefill_append(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" pkv_status pkv_paged_prefill_attention(const pkv_pool *pool, const void *q, const int32_t *block_tables,
+                                                  int32_t max_blocks_per_seq, const int32_t *cu_seqlens,
+                                                  const int32_t *start_pos, void *out, pkv_out_dtype out_dtype,
+                                                  int32_t batch, int32_t num_tokens, int32_t max_prompt_len,
+                                                  int32_t num_q_heads, float scale, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!(scale > 0.0f) || !isfinite(scale)) return PKV_ERR_SHAPE;
+  if (out_dtype != PKV_OUT_BF16 && out_dtype != PKV_OUT_F32) return PKV_ERR_SHAPE;
+  if (num_q_heads <= 0) return PKV_ERR_SHAPE;
+  if (pool && pool->num_kv_heads > 0 && num_q_heads != pkv::kGroup * pool->num_kv_heads) return PKV_ERR_UNSUPPORTED;
+  if (pool && batch > 0 && num_tokens > 0 && max_prompt_len > 0) {
+    if (!q || !out) return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out)) return PKV_ERR_ALIGNMENT;
+  }
+  pkv_status st = prefill_checks(pool, block_tables, max_blocks_per_seq, cu_seqlens, start_pos, batch, num_tokens,
+                                 max_prompt_len, s);
+  if (st != PKV_OK || batch == 0 || num_tokens == 0 || max_prompt_len == 0) return st;
+  pkv::PrefillParams p =
+      prefill_params(pool, block_tables, max_blocks_per_seq, cu_seqlens, start_pos, batch, num_tokens, max_prompt_len);
+  p.q = static_cast<const uint16_t *>(q);
+  p.out = out;
+  p.num_q_heads = num_q_heads;
+  p.score_log2 = scale * 1.4426950408889634f;
+  return pkv::launch_prefill_attention(p, out_dtype == PKV_OUT_BF16, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}

@@ -64,7 +64,31 @@ struct RopeAppendParams {
   int32_t num_q_heads;
 };
 
+// Paged prefill: sequence b owns packed rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of q / k_new /
+// v_new / out, and its prompt token i sits at absolute position start_pos[b] + i.
+struct PrefillParams {
+  const uint16_t *q;       // [num_tokens][num_q_heads][kHeadDim]
+  uint16_t *k_pool;        // [num_pages][num_kv_heads][kBlock][kHeadDim]
+  uint16_t *v_pool;
+  const int32_t *block_tables;  // [batch][max_blocks]
+  const int32_t *cu_seqlens;    // [batch + 1]
+  const int32_t *start_pos;     // [batch]
+  const uint16_t *k_new;   // [num_tokens][num_kv_heads][kHeadDim]
+  const uint16_t *v_new;
+  void *out;               // [num_tokens][num_q_heads][kHeadDim], FP32 or BF16
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t max_blocks;
+  int32_t batch;
+  int32_t max_prompt_len;  // bound on every prompt length: sets the grid
+  int32_t num_tokens;      // rows of q / k_new / v_new / out
+  float score_log2;
+};
+
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
+hipError_t launch_prefill_append(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_prefill_attention(const PrefillParams &p, bool out_bf16, hipStream_t stream);
 hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeParams &p, bool out_bf16, hipStream_t stream);
 

@@ -62,3 +62,33 @@ extern "C" pkv_status pkv_validate_decode_host(const int32_t *block_tables, int3
   }
   return PKV_OK;
 }
+
+extern "C" pkv_status pkv_validate_prefill_host(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                                const int32_t *cu_seqlens, const int32_t *start_pos, int32_t batch,
+                                                int32_t num_tokens, int32_t max_prompt_len, int32_t num_pages,
+                                                int32_t *bad_row) {
+  if (bad_row) *bad_row = -1;
+  if (batch < 0 || num_tokens < 0 || max_prompt_len < 0 || max_blocks_per_seq <= 0 || num_pages <= 0)
+    return PKV_ERR_SHAPE;
+  if (batch == 0) return PKV_OK;
+  if (!block_tables || !cu_seqlens || !start_pos) return PKV_ERR_NULL;
+  std::unordered_set<int64_t> targets;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t row0 = cu_seqlens[b], end = cu_seqlens[b + 1], start = start_pos[b];
+    const int64_t n = end - row0;
+    bool ok = row0 >= 0 && n >= 0 && end <= num_tokens && n <= max_prompt_len && start >= 0 &&
+              start + n <= (int64_t)max_blocks_per_seq * kBlock;
+    if (ok) {
+      const int32_t *row = block_tables + (int64_t)b * max_blocks_per_seq;
+      const int64_t need = (start + n + kBlock - 1) / kBlock;
+      for (int64_t e = 0; ok && e < need; ++e) ok = row[e] >= 0 && row[e] < num_pages;
+      for (int64_t pos = start; ok && pos < start + n; ++pos)
+        ok = targets.insert((int64_t)row[pos / kBlock] * kBlock + pos % kBlock).second;
+    }
+    if (!ok) {
+      if (bad_row) *bad_row = b;
+      return PKV_ERR_VALIDATION;
+    }
+  }
+  return PKV_OK;
+}

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     assert lib.pkv_abi_version() == 1
-    for code in range(8):
+    for code in range(11):
         assert lib.pkv_status_string(code)
     assert b"aligned" in lib.pkv_status_string(ALIGN)
 
@@ -165,6 +165,53 @@ def test_host_validators():
     bt2[1, 0] = 6
     assert pkv.validate_append_host(bt2, [19, 3, 63], 8) == (VALID, 1)  # same (page 6, slot 3) twice
     assert pkv.validate_append_host(bt2, [19, 4, 63], 8) == (OK, -1)
+
+
+def test_prefill_host_checks(lib):
+    good = pkv.Pool(FAKE, FAKE, 8, 8, 64, 16)
+
+    def app(pool=ctypes.byref(good), bt=FAKE, maxb=128, cu=FAKE, sp=FAKE, k=FAKE, v=FAKE, batch=1, tokens=4, mpl=4):
+        return lib.pkv_prefill_kv_append(pool, bt, maxb, cu, sp, k, v, batch, tokens, mpl, None)
+
+    def att(pool=ctypes.byref(good), q=FAKE, cu=FAKE, out=FAKE, odt=0, batch=1, tokens=4, mpl=4, hq=32, scale=0.125):
+        return lib.pkv_paged_prefill_attention(pool, q, FAKE, 128, cu, FAKE, out, odt, batch, tokens, mpl, hq, scale,
+                                               None)
+
+    assert app(pool=None) == NULL
+    assert app(batch=-1) == SHAPE and app(tokens=-1) == SHAPE and app(mpl=-1) == SHAPE and app(maxb=0) == SHAPE
+    assert app(batch=70000) == SHAPE
+    assert app(pool=ctypes.byref(pkv.Pool(FAKE, FAKE, 8, 8, 128, 16))) == UNSUP
+    assert app(batch=0) == OK and app(tokens=0) == OK and app(mpl=0) == OK
+    assert app(cu=None) == NULL and app(k=None) == NULL and app(sp=None) == NULL
+    assert app(k=FAKE + 2) == ALIGN
+    assert app(pool=ctypes.byref(pkv.Pool(FAKE + 4, FAKE, 8, 8, 64, 16))) == ALIGN
+    assert att(pool=None) == NULL
+    assert att(scale=0.0) == SHAPE and att(scale=float("nan")) == SHAPE and att(odt=5) == SHAPE
+    assert att(hq=0) == SHAPE and att(hq=16) == UNSUP
+    assert att(batch=0) == OK
+    assert att(q=None) == NULL and att(cu=None) == NULL and att(out=None) == NULL
+    assert att(out=FAKE + 8) == ALIGN
+
+
+def test_prefill_validator():
+    bt = np.full((3, 4), -1, dtype=np.int32)
+    bt[0, :2] = [5, 6]
+    bt[1, :1] = [2]
+    bt[2, :4] = [0, 1, 3, 4]
+    cu, sp = [0, 20, 36, 100], [0, 0, 0]
+    assert pkv.validate_prefill_host(bt, cu, sp, 100, 64, 8) == (OK, -1)
+    assert pkv.validate_prefill_host(bt, cu, sp, 99, 64, 8) == (VALID, 2)  # rows past num_tokens
+    assert pkv.validate_prefill_host(bt, cu, sp, 100, 63, 8) == (VALID, 2)  # longer than the bound
+    assert pkv.validate_prefill_host(bt, [0, 20, 37, 100], sp, 100, 64, 8) == (VALID, 1)  # needs block 1 of row 1
+    assert pkv.validate_prefill_host(bt, cu, [0, 0, 1], 100, 64, 8) == (VALID, 2)  # runs past the table
+    assert pkv.validate_prefill_host(bt, cu, [-1, 0, 0], 100, 64, 8) == (VALID, 0)
+    assert pkv.validate_prefill_host(bt, [0, 20, 19, 100], sp, 100, 81, 8) == (VALID, 1)  # negative length
+    assert pkv.validate_prefill_host(bt, [0, 10, 26, 90], [10, 0, 0], 100, 64, 8) == (OK, -1)  # chunk behind 10
+    bt2 = bt.copy()
+    bt2[1, 0] = 6
+    # row 0 fills page 6 slots 0..3 (positions 16..19); row 1 writes one token into page 6
+    assert pkv.validate_prefill_host(bt2, [0, 20, 21, 22], [0, 4, 0], 22, 64, 8) == (OK, -1)
+    assert pkv.validate_prefill_host(bt2, [0, 20, 21, 22], [0, 3, 0], 22, 64, 8) == (VALID, 1)  # (page 6, slot 3) twice
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -1,0 +1,217 @@
+"""Paged prefill through the C ABI against the FP64 prefill oracle: the append bit for bit, the
+causal attention within the decode tolerance, at small sizes (every row) and at the 16 x 512
+launch (sampled rows), plus ragged lengths, cached prefixes and the error behaviour."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import assert_close, bf16_to_bits, to_gpu_bf16, to_gpu_i32
+from workloads import make_prefill, make_prefill_config
+
+pytestmark = pytest.mark.gpu
+NAN = np.uint16(0x7FC0)
+
+
+def upload(w):
+    return {
+        "k_pool": to_gpu_bf16(w.k_pool),
+        "v_pool": to_gpu_bf16(w.v_pool),
+        "block_tables": to_gpu_i32(w.block_tables),
+        "cu_seqlens": to_gpu_i32(w.cu_seqlens),
+        "start_pos": to_gpu_i32(w.start_pos),
+        "q": to_gpu_bf16(w.q),
+        "k_new": to_gpu_bf16(w.k_new),
+        "v_new": to_gpu_bf16(w.v_new),
+    }
+
+
+def run(gpu, d, out_dtype, max_prompt_len=None):
+    gpu.prefill_kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["cu_seqlens"], d["start_pos"], d["k_new"],
+                          d["v_new"], max_prompt_len=max_prompt_len)
+    return gpu.paged_prefill_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["cu_seqlens"],
+                                       d["start_pos"], out_dtype=out_dtype, max_prompt_len=max_prompt_len)
+
+
+@pytest.mark.parametrize("name", ["prefill_tiny", "prefill512", "prefill_chunked", "prefill16x512"])
+def test_prefill_matches_oracle(gpu, name):
+    import torch
+
+    w = make_prefill_config(name)
+    print(f"[prefill] config={name} B={w.batch} tokens={w.tokens}", flush=True)
+    d = upload(w)
+    out = run(gpu, d, torch.float32)
+    torch.cuda.synchronize()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, w.v_new)
+    assert np.array_equal(bf16_to_bits(d["k_pool"]), rk) and np.array_equal(bf16_to_bits(d["v_pool"]), rv)
+    if w.tokens <= 600:
+        rows = list(range(w.tokens))
+    else:  # the first, last and a spread of rows of every sequence
+        rng = np.random.default_rng(1)
+        rows = set()
+        for b in range(w.batch):
+            lo, hi = int(w.cu_seqlens[b]), int(w.cu_seqlens[b + 1])
+            rows |= {lo, hi - 1, *rng.integers(lo, hi, size=3).tolist()}
+        rows = sorted(rows)
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos, rows=rows)
+    got = out.cpu().numpy()
+    assert_close(got[rows], ref[rows], name)
+    # BF16 output is the round-to-nearest-even of the FP32 output
+    out_bf = gpu.paged_prefill_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["cu_seqlens"],
+                                         d["start_pos"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_bits(out_bf), bf16_to_bits(out.to(torch.bfloat16)))
+
+
+def test_prefill_ragged_lengths_and_prefixes(gpu):
+    import torch
+
+    lens = [1, 15, 16, 17, 31, 32, 33, 47, 64, 100]
+    starts = [0, 5, 16, 3, 0, 31, 32, 200, 1, 0]
+    w = make_prefill(21, lens, starts)
+    print(f"[prefill] ragged lens={lens} starts={starts}", flush=True)
+    d = upload(w)
+    out = run(gpu, d, torch.float32, max_prompt_len=128)  # a bound above every length
+    torch.cuda.synchronize()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, w.v_new)
+    assert np.array_equal(bf16_to_bits(d["k_pool"]), rk) and np.array_equal(bf16_to_bits(d["v_pool"]), rv)
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos)
+    assert_close(out.cpu().numpy(), ref, "ragged")
+
+
+def test_prefill_rows_equal_decode_kernel(gpu):
+    """Row i of a prefill is the decode attention at position start + i: both kernels agree
+    within twice the tolerance (each is within it of the same oracle value)."""
+    import torch
+
+    w = make_prefill(22, [70], [9])
+    d = upload(w)
+    out = run(gpu, d, torch.float32)
+    rows = np.arange(w.tokens)
+    bt = d["block_tables"].expand(len(rows), -1).contiguous()
+    lens = to_gpu_i32(9 + rows + 1)
+    dec = gpu.paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], bt, lens, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    a, b = out.cpu().numpy(), dec.cpu().numpy()
+    assert np.all(np.abs(a - b) <= 4e-3 + 2e-2 * np.abs(b))
+
+
+def test_prefill_ignores_stale_slots_and_unused_pages(gpu):
+    import torch
+
+    w = make_prefill(23, [40, 25], [10, 0])
+    k_pool, v_pool = w.k_pool.copy(), w.v_pool.copy()
+    used = set(int(p) for p in w.block_tables.ravel() if p >= 0)
+    for p in range(w.num_pages):
+        if p not in used:
+            k_pool[p] = NAN
+            v_pool[p] = NAN
+    for b in range(w.batch):  # NaN in every slot past each sequence's last position
+        last = int(w.start_pos[b]) + int(w.cu_seqlens[b + 1] - w.cu_seqlens[b]) - 1
+        page = int(w.block_tables[b, last // 16])
+        k_pool[page, :, last % 16 + 1:] = NAN
+        v_pool[page, :, last % 16 + 1:] = NAN
+    w.k_pool, w.v_pool = k_pool, v_pool
+    d = upload(w)
+    out = run(gpu, d, torch.float32).cpu().numpy()
+    rk, rv = oracle.prefill_kv_append(k_pool, v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, w.v_new)
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos)
+    assert_close(out, ref, "stale NaN")
+
+
+@pytest.mark.parametrize("bad", ["entry", "start", "past_table"])
+def test_prefill_invalid_sequence_gets_zeros(gpu, bad):
+    import torch
+
+    w = make_prefill(24, [20, 30, 18], [0, 4, 0], max_blocks=8)
+    bt, sp = w.block_tables.copy(), w.start_pos.copy()
+    if bad == "entry":
+        bt[1, 1] = w.num_pages  # needed by rows of sequence 1
+    elif bad == "start":
+        sp[1] = -1
+    else:
+        sp[1] = 8 * 16 - 29  # start + length runs one past the 8-entry table
+    d = upload(w)
+    d["block_tables"], d["start_pos"] = to_gpu_i32(bt), to_gpu_i32(sp)
+    out = gpu.paged_prefill_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["cu_seqlens"],
+                                      d["start_pos"], out_dtype=torch.float32).cpu().numpy()
+    lo, hi = int(w.cu_seqlens[1]), int(w.cu_seqlens[2])
+    assert np.all(out[lo:hi] == 0.0)
+    keep = np.r_[0:lo, hi:w.tokens]
+    ref = oracle.paged_prefill_attention(w.q, w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos,
+                                         rows=keep.tolist())
+    assert_close(out[keep], ref[keep], bad)
+
+
+def test_prefill_append_skips_rows_outside_the_table(gpu):
+    import torch
+
+    w = make_prefill(25, [20, 10], [0, 0], max_blocks=4)
+    bt = w.block_tables.copy()
+    bt[0, 1] = -1  # rows 16..19 of sequence 0 have no page
+    d = upload(w)
+    d["block_tables"] = to_gpu_i32(bt)
+    gpu.prefill_kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["cu_seqlens"], d["start_pos"], d["k_new"],
+                          d["v_new"])
+    torch.cuda.synchronize()
+    # the oracle on the rows that do have a page
+    cu = np.array([0, 16, 26], dtype=np.int32)
+    keep = np.r_[0:16, 20:30]
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, cu, w.start_pos, w.k_new[keep],
+                                      w.v_new[keep])
+    assert np.array_equal(bf16_to_bits(d["k_pool"]), rk) and np.array_equal(bf16_to_bits(d["v_pool"]), rv)
+
+
+def test_prefill_sequences_outside_the_bounds_are_untouched(gpu):
+    import torch
+
+    w = make_prefill(26, [20, 40, 8], [0, 0, 0])
+    d = upload(w)
+    sentinel = torch.full((w.tokens, 32, 64), 7.0, dtype=torch.float32, device=d["q"].device)
+    gpu.prefill_kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["cu_seqlens"], d["start_pos"], d["k_new"],
+                          d["v_new"], max_prompt_len=32)  # sequence 1 (40 rows) exceeds the bound
+    gpu.paged_prefill_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["cu_seqlens"], d["start_pos"],
+                                sentinel, max_prompt_len=32)
+    torch.cuda.synchronize()
+    out = sentinel.cpu().numpy()
+    assert np.all(out[20:60] == 7.0)
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables[[0, 2]], np.array([0, 20, 28]),
+                                      w.start_pos[[0, 2]], w.k_new[np.r_[0:20, 60:68]], w.v_new[np.r_[0:20, 60:68]])
+    assert np.array_equal(bf16_to_bits(d["k_pool"]), rk)
+    keep = np.r_[0:20, 60:68]
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos, rows=keep.tolist())
+    assert_close(out[keep], ref[keep], "bounded")
+
+
+def test_prefill_empty_inputs_are_no_ops(gpu):
+    import torch
+
+    w = make_prefill(27, [0, 5, 0], [0, 0, 3])
+    d = upload(w)
+    out = run(gpu, d, torch.float32)
+    torch.cuda.synchronize()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, w.v_new)
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos)
+    assert_close(out.cpu().numpy(), ref, "empty rows")
+    e = make_prefill(28, [0], [0])
+    de = upload(e)
+    out = run(gpu, de, torch.float32)
+    assert out.shape[0] == 0
+
+
+def test_prefill_debug_validation(gpu, monkeypatch):
+    import torch
+
+    w = make_prefill(29, [20, 20], [0, 0])
+    bt = w.block_tables.copy()
+    bt[1, 0] = bt[0, 0]  # both sequences write page bt[0, 0]
+    d = upload(w)
+    d["block_tables"] = to_gpu_i32(bt)
+    monkeypatch.setenv("PKV_DEBUG_VALIDATE", "1")
+    with pytest.raises(gpu.PagedKVError, match="VALIDATION"):
+        gpu.prefill_kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["cu_seqlens"], d["start_pos"],
+                              d["k_new"], d["v_new"])
+    d["block_tables"] = to_gpu_i32(w.block_tables)
+    out = run(gpu, d, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
