@@ -344,9 +344,63 @@ def run(args):
                 "figures are this build's measurements on one MI355X.",
     }
 
+    if not args.no_prefill:
+        result["prefill"] = prefill_leg(args, torch, pkv)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_min_seconds, args.cpu_max_seconds)
     print(json.dumps(result), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_leg(args, torch, pkv):
+    """The second workload: paged prefill (prompt K/V append, then causal attention over the
+    pages) on ``--prefill-config``.  Reported beside the decode step, never as ``value``.
+    Algorithmic flops: every visible (query, key) pair costs 2*64 for q.k and 2*64 for p*v, per
+    query head."""
+    from workloads import make_prefill_config
+
+    w = make_prefill_config(args.prefill_config)
+    dev_bf16 = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    dev_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    kp, vp = dev_bf16(w.k_pool), dev_bf16(w.v_pool)
+    bt, cu, sp = dev_i32(w.block_tables), dev_i32(w.cu_seqlens), dev_i32(w.start_pos)
+    q, kn, vn = dev_bf16(w.q), dev_bf16(w.k_new), dev_bf16(w.v_new)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    mpl = int(w.prompt_lens.max())
+    append = lambda: pkv.prefill_kv_append(kp, vp, bt, cu, sp, kn, vn, max_prompt_len=mpl)
+    attend = lambda: pkv.paged_prefill_attention(q, kp, vp, bt, cu, sp, out, max_prompt_len=mpl)
+    for _ in range(args.warmup):
+        append()
+        attend()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        append()
+        e[1].record()
+        attend()
+        e[2].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / K
+    app_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    pairs = int(w.meta["causal_pairs"])
+    flops = pairs * w.q.shape[1] * 4 * w.q.shape[2]
+    tflops = flops / (att_ms * 1e-3) / 1e12
+    return {
+        "workload": f"{args.prefill_config}: {w.batch} prompts, {w.tokens} query rows, start {int(w.start_pos.max())}",
+        "ms_per_step": round(wall_ms, 5),
+        "append_us": round(app_ms * 1e3, 3),
+        "attention_us": round(att_ms * 1e3, 3),
+        "tokens_per_s": round(w.tokens / (wall_ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_attention_kernel", "algorithmic_flops_per_launch": flops},
+    }
 
 
 def main():
@@ -360,6 +414,9 @@ def main():
     ap.add_argument("--graph", action="store_true", help="time the step as one captured HIP graph")
     ap.add_argument("--step", choices=["fused", "two-call"], default="fused",
                     help="which form of the step gives value/roofline (both are timed and reported)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the paged prefill measurement")
+    ap.add_argument("--prefill-config", default="prefill16x512",
+                    choices=["prefill_tiny", "prefill512", "prefill_chunked", "prefill16x512"])
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0, help="repeat CPU oracle passes at least this long")
     ap.add_argument("--cpu-max-seconds", type=float, default=30.0, help="hard bound on the CPU oracle timing")
     args = ap.parse_args()

@@ -23,6 +23,10 @@ LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
 HIP_SOURCES = ["pagedkv_api.hip", "kv_append.hip", "paged_attention.hip", "rope_append.hip", "prefill.hip"]
 CXX_SOURCES = ["validate.cpp", "page_allocator.cpp"]
 
+# Per-file additions.  prefill.hip: keep MFMA accumulators in ordinary VGPRs, so the softmax
+# rescale of the output tile does not copy it between register files every step.
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIP_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -66,7 +70,7 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(OBJ_DIR, src + ".o")
-        jobs.append([hipcc, *HIP_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *HIP_FLAGS, *FILE_FLAGS.get(src, []), *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in CXX_SOURCES:
         obj = os.path.join(OBJ_DIR, src + ".o")
         jobs.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj])

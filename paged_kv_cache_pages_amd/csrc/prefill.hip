@@ -6,7 +6,7 @@
 // The article materialises a [tokens][tokens] BF16 score matrix per head, masks it, runs a
 // softmax kernel over it and multiplies by V with library GEMMs.  Here no score matrix exists:
 // a workgroup owns 16 query rows of one sequence and the 4 query heads of one KV head (one head
-// per wavefront), streams the sequence's pages 32 keys at a time through LDS, and runs both
+// per wavefront), streams the sequence's pages 64 keys at a time through LDS, and runs both
 // products on the matrix cores (v_mfma_f32_16x16x32_bf16) with an FP32 online softmax in between.
 //
 // Register layout of the 16x16x32 BF16 MFMA on gfx950 (lane l, element i):
@@ -14,12 +14,14 @@
 //   B operand: column l % 16, reduction index 8 (l / 16) + i
 //   C/D:       column l % 16, row 4 (l / 16) + i
 // Scores are computed transposed, S^T = K Q^T (rows = keys, columns = the 16 queries), with the
-// 16 A-operand rows of key tile t mapped to keys 8 (r / 4) + 4 t + r % 4 of the 32-key step.
-// Then lane l holds, for query l % 16, exactly keys 8 (l / 16) .. 8 (l / 16) + 7 of the step in
+// 16 A-operand rows of key tile t mapped to keys 8 (r / 4) + 4 t + r % 4 of a 32-key half step.
+// Then lane l holds, for query l % 16, exactly keys 8 (l / 16) .. 8 (l / 16) + 7 of the half in
 // its two C tiles, which is the B-operand layout of P^T in O^T = V^T P^T: the probabilities
 // never leave their registers.  V is staged transposed in LDS so that V^T rows are contiguous.
 // The probabilities enter the second product as two BF16 terms (hi + lo), so the weights keep
 // about 16 significant bits; Q, K and V are BF16 inputs and are exact in the products.
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -28,13 +30,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kTileQ = 16;                 // query rows per workgroup
-constexpr int kChunk = 32;                 // keys per step (two pages)
+constexpr int kChunk = 64;                 // keys per step (four pages), two 32-key halves
 constexpr int kVecPerRow = kHeadDim * 2 / 16;  // 16-byte vectors per 64-wide BF16 row
 constexpr int kKStride = kHeadDim + 8;     // BF16 elements per staged K row (144 bytes)
-constexpr int kVStride = kChunk + 8;       // BF16 elements per staged V^T row (80 bytes)
+constexpr int kVStride = kChunk + 8;       // BF16 elements per staged V^T row (144 bytes)
 
 // Packed rows of sequence b, or false when they fall outside [0, num_tokens) or exceed the
 // prompt-length bound the grid was sized for (such a sequence is left untouched).
@@ -90,16 +94,23 @@ __device__ __forceinline__ void store_row4(void *out, int64_t elem, f32x4 v) {
   }
 }
 
-// grid = (num_kv_heads, batch, ceil(max_prompt_len / 16)); the query tile runs backwards in z so
-// the workgroups with the most keys are dispatched first.
+// One workgroup per (sequence, KV head, 16-row query tile), 1-D grid.  The query tile is the slowest
+// index and runs backwards, so the workgroups with the most keys are dispatched first and the
+// light ones fill the tail.  (Grouping a sequence's tiles on one XCD for L2 reuse was slower: it
+// gives up that order and unbalances the XCDs when prompts differ in length.)
+constexpr int kLdsPages = 256;  // block-table entries kept in LDS (4096 tokens); the rest from HBM
+
 template <bool kOutBf16>
-__global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillParams p, int32_t tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kChunk * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kHeadDim * kVStride];
+  __shared__ int32_t s_pages[kLdsPages];
 
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tile = (int)(gridDim.z - 1 - blockIdx.z);
+  const uint32_t pairs = gridDim.x / (uint32_t)tiles;  // batch * num_kv_heads
+  const int tile = tiles - 1 - (int)(blockIdx.x / pairs);
+  const uint32_t pair = blockIdx.x % pairs;  // b * num_kv_heads + g
+  const int g = (int)(pair % (uint32_t)p.num_kv_heads);
+  const int b = (int)(pair / (uint32_t)p.num_kv_heads);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int h = g * kGroup + (tid >> 6);  // one query head per wavefront
@@ -121,9 +132,10 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
     for (int e = tid; e < need; e += kThreads) {
       const int32_t pg = table[e];
       bad |= pg < 0 || pg >= p.num_pages;
+      if (e < kLdsPages) s_pages[e] = pg;
     }
   }
-  bad = __syncthreads_or(bad);
+  bad = __syncthreads_or(bad);  // also publishes s_pages
   const int64_t out_row = (int64_t)row0 + q_lo + r;  // this lane's output row
   if (bad) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -145,104 +157,153 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
     qf[1] = src[4 + j];
   }
 
-  // Staging: thread -> key (tid % 32) of the step and dims 8 (tid / 32) .. + 7.
-  const int st_key = tid & 31;
-  const int st_dim = (tid >> 5) * 8;
-  auto load_step = [&](int c, u32x4 &kr, u32x4 &vr) {
+  // Staging: thread -> key (tid % 64) of the step, dims d0 .. d0 + 7 and d0 + 32 .. d0 + 39 with
+  // d0 = 8 (tid / 64).
+  const int st_key = tid & 63;
+  const int st_dim = (tid >> 6) * 8;
+  // Page ids run one step ahead of the data: the id of step c + 1 is in hand when that step's K/V
+  // loads issue, so no load inside a step waits on another.  A key past the tile's last query
+  // reads the sequence's first page instead (validated, so in bounds); its V row is zeroed when
+  // staged and its score is masked.
+  auto page_of = [&](int c) -> int32_t {
     const int kp = c * kChunk + st_key;
-    kr = u32x4{0, 0, 0, 0};
-    vr = u32x4{0, 0, 0, 0};
-    if (kp < n_keys) {  // keys past the tile's last query stay zero (no stale NaN reaches V)
-      const int32_t pg = table[kp / kBlock];
-      const int64_t off = (((int64_t)pg * p.num_kv_heads + g) * kBlock + kp % kBlock) * kHeadDim + st_dim;
-      kr = *reinterpret_cast<const u32x4 *>(p.k_pool + off);
-      vr = *reinterpret_cast<const u32x4 *>(p.v_pool + off);
+    const int e = kp < n_keys ? kp / kBlock : 0;
+    return e < kLdsPages ? s_pages[e] : table[e];
+  };
+  struct Rows {
+    u32x4 k[2], v[2];
+  };
+  auto load_step = [&](int c, int32_t pg, Rows &x) {
+    const int kp = c * kChunk + st_key;
+    const int64_t off = (((int64_t)pg * p.num_kv_heads + g) * kBlock + kp % kBlock) * kHeadDim + st_dim;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      x.k[e] = *reinterpret_cast<const u32x4 *>(p.k_pool + off + 32 * e);
+      x.v[e] = *reinterpret_cast<const u32x4 *>(p.v_pool + off + 32 * e);
     }
   };
-  auto stage = [&](int buf, const u32x4 &kr, const u32x4 &vr) {
-    *reinterpret_cast<u32x4 *>(&s_k[buf][st_key * kKStride + st_dim]) = kr;
-    uint16_t *vt = &s_vt[buf][st_dim * kVStride + st_key];
+  auto stage = [&](int c, int buf, Rows &x) {
+    if (c * kChunk + kChunk > n_keys && c * kChunk + st_key >= n_keys)  // no stale NaN reaches V
+      x.v[0] = x.v[1] = u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vt[(2 * e) * kVStride] = (uint16_t)(vr[e] & 0xFFFFu);
-      vt[(2 * e + 1) * kVStride] = (uint16_t)(vr[e] >> 16);
+    for (int e = 0; e < 2; ++e) {
+      *reinterpret_cast<u32x4 *>(&s_k[buf][st_key * kKStride + st_dim + 32 * e]) = x.k[e];
+      uint16_t *vt = &s_vt[buf][(st_dim + 32 * e) * kVStride + st_key];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vt[(2 * w) * kVStride] = (uint16_t)(x.v[e][w] & 0xFFFFu);
+        vt[(2 * w + 1) * kVStride] = (uint16_t)(x.v[e][w] >> 16);
+      }
     }
   };
 
-  u32x4 kr, vr;
-  load_step(0, kr, vr);
-  stage(0, kr, vr);
+  Rows rows;
+  load_step(0, page_of(0), rows);
+  int32_t pg_next = page_of(1);
+  stage(0, 0, rows);
   __syncthreads();
 
   f32x4 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;  // running max in log2 units, shared by the 4 lanes of a query
-  float l = 0.f;        // this lane's part of the denominator
+  // Softmax anchor in log2 units, shared by the 4 lanes of a query.  It moves only when a score
+  // exceeds it by more than kHeadroom, so most steps leave the accumulators alone; weights are
+  // then at most 2^kHeadroom, far inside FP32 and the hi + lo BF16 split.
+  constexpr float kHeadroom = 8.0f;
+  float m = -INFINITY;
+  float l = 0.f;  // this lane's part of the denominator
   const float c_log2 = p.score_log2;
+  const int first_q = start + q_lo;  // smallest query position of the tile
 
-  for (int c = 0; c < n_chunks; ++c) {
-    const int buf = c & 1;
+  // One step; `buf` is a compile-time constant at both call sites (the loop is unrolled by two),
+  // so every LDS address of the step is a register base plus an immediate offset.
+  auto step = [&](int c, auto buf_tag) {
+    constexpr int buf = decltype(buf_tag)::value;
     const bool more = c + 1 < n_chunks;
-    if (more) load_step(c + 1, kr, vr);  // in flight while this step computes
-
-    // S^T for the two key tiles of the step.
-    f32x4 s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int key_row = 8 * (r >> 2) + 4 * t + (r & 3);
-      const uint16_t *krow = &s_k[buf][key_row * kKStride + 8 * j];
-      const u32x4 k0 = *reinterpret_cast<const u32x4 *>(krow);
-      const u32x4 k1 = *reinterpret_cast<const u32x4 *>(krow + 32);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), as_bf16x8(qf[0]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), as_bf16x8(qf[1]), acc, 0, 0, 0);
-      s[t] = acc;
+    if (more) {  // in flight while this step computes
+      load_step(c + 1, pg_next, rows);
+      pg_next = page_of(c + 2);
     }
 
-    // Causal mask and the online softmax (scores in log2 units).
-    const int key0 = c * kChunk + 8 * j;  // keys key0 + 4 t + i
-    float x[8];
+    // S^T for the four 16-key tiles of the step: half hs, tile t.
+    f32x4 s[2][2];
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int key_row = 32 * hs + 8 * (r >> 2) + 4 * t + (r & 3);
+        const uint16_t *krow = &s_k[buf][key_row * kKStride + 8 * j];
+        const u32x4 k0 = *reinterpret_cast<const u32x4 *>(krow);
+        const u32x4 k1 = *reinterpret_cast<const u32x4 *>(krow + 32);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), as_bf16x8(qf[0]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), as_bf16x8(qf[1]), acc, 0, 0, 0);
+        s[hs][t] = acc;
+      }
+
+    // Causal mask, only on steps that reach past the tile's first query.
+    if (c * kChunk + kChunk - 1 > first_q) {
+      const int room = q_pos - (c * kChunk + 8 * j);  // this lane holds keys q_pos - room + 32 hs + 4 t + i
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (32 * hs + 4 * t + i > room) s[hs][t][i] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool visible = key0 + 4 * t + i <= q_pos;
-        const float v = visible ? s[t][i] * c_log2 : -INFINITY;
-        x[4 * t + i] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int t = 0; t < 2; ++t)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[hs][t][0], s[hs][t][1]), fmaxf(s[hs][t][2], s[hs][t][3])));
     mx = wave_xor_max(mx, 16);
     mx = wave_xor_max(mx, 32);
-    const float m_new = fmaxf(m, mx);  // finite: key 0 is visible to every query
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    l *= alpha;
+    mx *= c_log2;  // scale > 0; -inf stays -inf.  Finite after step 0: key 0 is visible to all.
+    if (__builtin_amdgcn_ballot_w64(mx > m + kHeadroom)) {  // wave-uniform
+      const float m_new = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-    // Each weight is carried as a sum of two BF16 values (hi + lo, ~16 significant bits): with a
-    // single BF16 weight a short context keeps the 2^-9 rounding of its few large weights.
-    bf16x8 ph, pl;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(x[e] - m);
-      l += pe;
-      const __bf16 hi = (__bf16)pe;
-      ph[e] = hi;
-      pl[e] = (__bf16)(pe - (float)hi);  // the difference is exact in FP32
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
 
-    // O^T += V^T P^T, one 16-dim tile at a time.
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const u32x4 vf = *reinterpret_cast<const u32x4 *>(&s_vt[buf][(16 * dt + r) * kVStride + 8 * j]);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), ph, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), pl, o[dt], 0, 0, 0);
+    for (int hs = 0; hs < 2; ++hs) {
+      // Each weight is carried as a sum of two BF16 values (hi + lo, ~16 significant bits): with
+      // a single BF16 weight a short context keeps the 2^-9 rounding of its few large weights.
+      u32x4 ph, pl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f2 pe;
+        pe[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hs][e >> 1][2 * (e & 1)], c_log2, -m));
+        pe[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hs][e >> 1][2 * (e & 1) + 1], c_log2, -m));
+        l += pe[0] + pe[1];
+        const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(pe, b2));
+        ph[e] = hi;
+        f2 rest;  // exact in FP32: each value minus its own BF16 rounding
+        rest[0] = pe[0] - __builtin_bit_cast(float, hi << 16);
+        rest[1] = pe[1] - __builtin_bit_cast(float, hi & 0xFFFF0000u);
+        pl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, b2));
+      }
+      // O^T += V^T P^T, one 16-dim tile at a time.
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const u32x4 vf =
+            *reinterpret_cast<const u32x4 *>(&s_vt[buf][(16 * dt + r) * kVStride + 32 * hs + 8 * j]);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(ph), o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pl), o[dt], 0, 0, 0);
+      }
     }
 
-    if (more) stage(buf ^ 1, kr, vr);
+    if (more) stage(c + 1, buf ^ 1, rows);
     __syncthreads();
+  };
+  for (int c = 0; c < n_chunks; c += 2) {
+    step(c, std::integral_constant<int, 0>{});
+    if (c + 1 < n_chunks) step(c + 1, std::integral_constant<int, 1>{});
   }
 
   l += __shfl_xor(l, 16, 64);
@@ -267,13 +328,15 @@ hipError_t launch_prefill_append(const PrefillParams &p, hipStream_t stream) {
 
 hipError_t launch_prefill_attention(const PrefillParams &p, bool out_bf16, hipStream_t stream) {
   const int64_t tiles = ((int64_t)p.max_prompt_len + kTileQ - 1) / kTileQ;
-  if (tiles == 0 || p.batch == 0) return hipSuccess;
-  if (tiles > 65535 || p.batch > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)p.num_kv_heads, (unsigned)p.batch, (unsigned)tiles);
+  const int64_t blocks = tiles * p.batch * p.num_kv_heads;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (out_bf16)
-    hipLaunchKernelGGL(prefill_attention_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(prefill_attention_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p,
+                       (int32_t)tiles);
   else
-    hipLaunchKernelGGL(prefill_attention_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(prefill_attention_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p,
+                       (int32_t)tiles);
   return hipGetLastError();
 }
 
