@@ -33,6 +33,8 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "paged decode attention GB/s and % of HBM peak; seq-tokens attended/sec"
 ATTN_SOURCE = os.path.join(ROOT, "paged_kv_cache_pages_amd", "csrc", "paged_attention.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_bw256_traffic.md")
+PREFILL_SOURCE = os.path.join(ROOT, "paged_kv_cache_pages_amd", "csrc", "prefill.hip")
+PREFILL_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_prefill_16x512_traffic.md")
 
 WORKLOAD_TEXT = {
     "tiny": "1 sequence, context 37 (3 pages, last partial), 8-page pool",
@@ -70,10 +72,10 @@ def seq_tokens(w) -> int:
 # HBM traffic measured with rocprofv3 counters (taken offline, recorded under profiles/)
 # ---------------------------------------------------------------------------------------------
 
-def kernel_source_digest() -> str:
-    """Hash of the attention kernel's code with comments and whitespace removed, so the recorded
+def kernel_source_digest(path: str = ATTN_SOURCE) -> str:
+    """Hash of a kernel source's code with comments and whitespace removed, so the recorded
     counters stay valid across comment-only edits and lapse on any code change."""
-    with open(ATTN_SOURCE) as f:
+    with open(path) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
@@ -81,15 +83,15 @@ def kernel_source_digest() -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def recorded_traffic(tag: str):
-    """Traffic per launch of the ``tag`` kernel ("attention" or "fused") from the committed counter
-    summary, or None when the kernel source has changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_PROFILE):
+def recorded_traffic(tag: str, profile: str = TRAFFIC_PROFILE, source: str = ATTN_SOURCE):
+    """Traffic per launch of the ``tag`` kernel from a committed counter summary, or None when the
+    kernel source has changed since the counters were taken."""
+    if not os.path.exists(profile):
         return None
-    text = open(TRAFFIC_PROFILE).read()
+    text = open(profile).read()
     m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_val = re.search(r"traffic_bytes_per_launch\[" + tag + r"\]:\s*([0-9.eE+]+)", text)
-    if not (m_src and m_val) or m_src.group(1) != kernel_source_digest():
+    if not (m_src and m_val) or m_src.group(1) != kernel_source_digest(source):
         return None
     return float(m_val.group(1))
 
@@ -376,18 +378,26 @@ def prefill_leg(args, torch, pkv):
         attend()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+
+    def back_to_back(fn):
+        """Mean ms per launch of K launches queued back to back between two events (the GPU
+        never waits for the host, so this is the kernel's own duration plus the queue gap)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
     t0 = time.perf_counter()
-    for e in ev:
-        e[0].record()
+    for _ in range(K):
         append()
-        e[1].record()
         attend()
-        e[2].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / K
-    app_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    app_ms = back_to_back(append)  # the append rewrites the same rows: repeatable
+    att_ms = back_to_back(attend)
     pairs = int(w.meta["causal_pairs"])
     flops = pairs * w.q.shape[1] * 4 * w.q.shape[2]
     tflops = flops / (att_ms * 1e-3) / 1e12
@@ -398,7 +408,9 @@ def prefill_leg(args, torch, pkv):
         "attention_us": round(att_ms * 1e3, 3),
         "tokens_per_s": round(w.tokens / (wall_ms * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic("prefill_attention", PREFILL_TRAFFIC_PROFILE, PREFILL_SOURCE)
+                     if args.prefill_config == "prefill16x512" else None,
                      "kernel": "prefill_attention_kernel", "algorithmic_flops_per_launch": flops},
     }
 
