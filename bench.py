@@ -380,12 +380,24 @@ def prefill_leg(args, torch, pkv):
     K = args.steps
 
     def back_to_back(fn):
-        """Mean ms per launch of K launches queued back to back between two events (the GPU
-        never waits for the host, so this is the kernel's own duration plus the queue gap)."""
+        """Mean ms per launch of K launches captured in one HIP graph and replayed between two
+        events: the GPU never waits for the host, so this is the kernel's own duration plus the
+        gap between graph nodes (the append alone is shorter than a Python-side launch)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(K):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(K):
-            fn()
+        graph.replay()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K
