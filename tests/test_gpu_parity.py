@@ -323,3 +323,22 @@ def test_batch_zero_is_a_no_op(gpu):
     out = gpu.paged_decode_attention(e((0, 32, 64), dtype=torch.bfloat16, device="cuda"), kp, kp,
                                      e((0, 8), dtype=torch.int32, device="cuda"), e((0,), dtype=torch.int32, device="cuda"))
     assert out.shape == (0, 32, 64)
+
+
+def test_one_workspace_serves_every_shape(gpu):
+    """Calls of different shapes and split sizes share one workspace (as the binding's per-stream
+    cache does), twice over: every result matches the oracle whatever the workspace held."""
+    import torch
+
+    cases = [(make_custom(seed=32, lengths=[2048] * 3 + [40]), 8), (make_custom(seed=33, lengths=[1500]), 4),
+             (make_custom(seed=34, lengths=[700, 1, 2000, 64, 900]), 12), (make_custom(seed=35, lengths=[2048]), 4)]
+    nbytes = max(gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, pp) for w, pp in cases)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")  # garbage (NaN-ish) contents
+    for rnd in range(2):
+        for w, pp in cases:
+            d = upload(w)
+            out = gpu.paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                                             out_dtype=torch.float32, partition_pages=pp, workspace=ws)
+            torch.cuda.synchronize()
+            ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens)
+            assert_close(out.cpu().numpy(), ref, f"round {rnd} B={w.batch} pp={pp}")
