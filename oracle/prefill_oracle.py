@@ -47,26 +47,26 @@ def prefill_kv_append(k_pool, v_pool, block_tables, cu_seqlens, start_pos, k_new
     return k_out, v_out
 
 
-def causal_attention_rows(q, keys, values, start, scale):
-    """Causal attention of ``n`` query rows at positions ``start .. start + n - 1``.
+def causal_attention_rows(q, keys, values, positions, scale):
+    """Causal attention of query rows at absolute ``positions``.
 
-    ``q`` FP64 [n][Hq][D]; ``keys``/``values`` FP64 [start + n][Hkv][D] (all positions up to the
-    last query).  Row ``i`` sees keys ``0 .. start + i`` only: the excluded cells have probability
-    0, so the row is computed over its visible prefix alone and later rows cannot reach it.
+    ``q`` FP64 [n][Hq][D]; ``keys``/``values`` FP64 [L][Hkv][D] with L > max(positions).  Row ``i``
+    sees keys ``0 .. positions[i]`` only: the excluded cells have probability 0, so the row is
+    computed over its visible prefix alone and later rows cannot reach it.
     """
     n, hq, d = q.shape
     group = hq // keys.shape[1]
-    kv_of = np.array([kv_head_of(h, group) for h in range(hq)])
+    k_heads = np.ascontiguousarray(keys.transpose(1, 0, 2))  # [Hkv][L][D]: one head's rows contiguous
+    v_heads = np.ascontiguousarray(values.transpose(1, 0, 2))
     out = np.empty((n, hq, d), dtype=np.float64)
     for i in range(n):
-        visible = start + i + 1
-        k = keys[:visible][:, kv_of, :]  # [visible][Hq][D], KV head h // 4 for query head h
-        v = values[:visible][:, kv_of, :]
-        scores = np.einsum("hd,lhd->hl", q[i], k) * scale
-        m = scores.max(axis=1, keepdims=True)
-        w = np.exp(scores - m)
-        probs = w / w.sum(axis=1, keepdims=True)
-        out[i] = np.einsum("hl,lhd->hd", probs, v)
+        visible = int(positions[i]) + 1
+        for h in range(hq):
+            g = kv_head_of(h, group)
+            scores = (k_heads[g, :visible] @ q[i, h]) * scale
+            m = scores.max()
+            w = np.exp(scores - m)
+            out[i, h] = (w / w.sum()) @ v_heads[g, :visible]
     return out
 
 
@@ -83,11 +83,11 @@ def paged_prefill_attention(q, k_pool, v_pool, block_tables, cu_seqlens, start_p
         if not sel:
             continue
         start = int(start_pos[b])
-        L = start + max(sel) - lo + 1
+        positions = np.array([start + r - lo for r in sel])
+        L = int(positions.max()) + 1
         keys = bf16_bits_to_f64(gather_context(k_pool, block_tables[b], L))
         values = bf16_bits_to_f64(gather_context(v_pool, block_tables[b], L))
-        for r in sel:
-            out[r] = causal_attention_rows(bf16_bits_to_f64(q[r:r + 1]), keys, values, start + r - lo, scale)[0]
+        out[sel] = causal_attention_rows(bf16_bits_to_f64(q[sel]), keys, values, positions, scale)
     return out
 
 

@@ -8,7 +8,7 @@ from hypothesis import given, settings
 from hypothesis import strategies as st
 
 import oracle
-from gpu_helpers import assert_close, bf16_to_bits, to_gpu_i32, upload
+from gpu_helpers import assert_close, bf16_to_bits, to_gpu_bf16, to_gpu_i32, upload
 from workloads import make_custom
 
 pytestmark = pytest.mark.gpu
@@ -38,3 +38,34 @@ def test_random_steps(gpu, lengths, hkv, partition_pages, seed):
     assert np.array_equal(bf16_to_bits(k2), rk) and np.array_equal(bf16_to_bits(v2), rv)
     ref = oracle.paged_decode_attention(w.q[0], rk, rv, w.block_tables[0], w.context_lens)
     assert_close(b.cpu().numpy(), ref, f"lengths={lengths} hkv={hkv} pp={partition_pages}")
+
+
+@settings(max_examples=15, deadline=None, derandomize=True)
+@given(
+    lengths=st.lists(st.integers(0, 200), min_size=1, max_size=5),
+    starts=st.lists(st.integers(0, 700), min_size=5, max_size=5),
+    seed=st.integers(0, 2**16),
+)
+def test_random_prefill_steps(gpu, lengths, starts, seed):
+    """Random prompt batches (empty prompts, chunks behind cached prefixes of any offset) through
+    the prefill pair, against the prefill oracle."""
+    import torch
+
+    from workloads import make_prefill
+
+    starts = starts[: len(lengths)]
+    w = make_prefill(seed, lengths, starts)
+    if w.tokens == 0:
+        return
+    d = {"block_tables": to_gpu_i32(w.block_tables), "cu_seqlens": to_gpu_i32(w.cu_seqlens),
+         "start_pos": to_gpu_i32(w.start_pos)}
+    kp, vp = to_gpu_bf16(w.k_pool), to_gpu_bf16(w.v_pool)
+    gpu.prefill_kv_append(kp, vp, d["block_tables"], d["cu_seqlens"], d["start_pos"], to_gpu_bf16(w.k_new),
+                          to_gpu_bf16(w.v_new))
+    out = gpu.paged_prefill_attention(to_gpu_bf16(w.q), kp, vp, d["block_tables"], d["cu_seqlens"], d["start_pos"],
+                                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, w.v_new)
+    assert np.array_equal(bf16_to_bits(kp), rk) and np.array_equal(bf16_to_bits(vp), rv)
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos)
+    assert_close(out.cpu().numpy(), ref, f"lengths={lengths} starts={starts}")
