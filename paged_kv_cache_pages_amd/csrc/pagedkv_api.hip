@@ -382,5 +382,7 @@ extern "C" pkv_status pkv_paged_prefill_attention(const pkv_pool *pool, const vo
   p.out = out;
   p.num_q_heads = num_q_heads;
   p.score_log2 = scale * 1.4426950408889634f;
-  return pkv::launch_prefill_attention(p, out_dtype == PKV_OUT_BF16, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  const int32_t cus = pkv_device_cu_count();
+  if (cus <= 0) return PKV_ERR_HIP;
+  return pkv::launch_prefill_attention(p, out_dtype == PKV_OUT_BF16, cus, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

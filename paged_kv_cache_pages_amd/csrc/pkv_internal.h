@@ -88,7 +88,7 @@ struct PrefillParams {
 
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_prefill_append(const PrefillParams &p, hipStream_t stream);
-hipError_t launch_prefill_attention(const PrefillParams &p, bool out_bf16, hipStream_t stream);
+hipError_t launch_prefill_attention(const PrefillParams &p, bool out_bf16, int32_t num_cus, hipStream_t stream);
 hipError_t launch_rope_append(const RopeAppendParams &p, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeParams &p, bool out_bf16, hipStream_t stream);
 

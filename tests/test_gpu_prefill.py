@@ -79,6 +79,26 @@ def test_prefill_ragged_lengths_and_prefixes(gpu):
     assert_close(out.cpu().numpy(), ref, "ragged")
 
 
+def test_prefill_many_ragged_prompts(gpu):
+    """Enough prompts that the launch takes two 16-query blocks per wavefront (at least two
+    workgroups per compute unit), with ragged lengths so the second block is often partial."""
+    import torch
+
+    rng = np.random.default_rng(40)
+    lens = [int(x) for x in rng.integers(1, 200, size=24)] + [1, 16, 17, 32, 33]
+    starts = [int(x) for x in rng.integers(0, 600, size=len(lens))]
+    w = make_prefill(41, lens, starts)
+    print(f"[prefill] many ragged prompts B={w.batch} tokens={w.tokens}", flush=True)
+    d = upload(w)
+    out = run(gpu, d, torch.float32)
+    torch.cuda.synchronize()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, w.v_new)
+    assert np.array_equal(bf16_to_bits(d["k_pool"]), rk) and np.array_equal(bf16_to_bits(d["v_pool"]), rv)
+    rows = sorted(set(np.random.default_rng(2).integers(0, w.tokens, size=400).tolist()))
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos, rows=rows)
+    assert_close(out.cpu().numpy()[rows], ref[rows], "many ragged")
+
+
 def test_prefill_rows_equal_decode_kernel(gpu):
     """Row i of a prefill is the decode attention at position start + i: both kernels agree
     within twice the tolerance (each is within it of the same oracle value)."""
