@@ -58,6 +58,14 @@ def attention_bytes(w) -> int:
     return per_layer * w.layers
 
 
+def attention_bytes_token_exact(w) -> int:
+    """As attention_bytes, with K/V counted per attended token (L x 2 KiB) instead of whole pages."""
+    hq, d, hkv = w.num_q_heads, w.head_dim, w.num_kv_heads
+    pages = int(np.sum((w.context_lens.astype(np.int64) + 15) // 16))
+    per_layer = w.batch * (hq * d * 2) * 2 + int(w.context_lens.sum()) * (2 * hkv * d * 2) + pages * 4
+    return per_layer * w.layers
+
+
 def append_bytes(w) -> int:
     """k_new + v_new read, the same rows written, one position and one table entry per row."""
     row = w.num_kv_heads * w.head_dim * 2
@@ -101,14 +109,13 @@ def recorded_traffic(tag: str, profile: str = TRAFFIC_PROFILE, source: str = ATT
 # ---------------------------------------------------------------------------------------------
 
 def cpu_baseline(w, min_seconds: float, max_seconds: float):
-    """Time the oracle's append + attention on the same workload, on the host.
+    """Time the oracle's append + attention on the same workload, on one host core.
 
     Whole passes over the batch (append of every layer, then attention of every sequence and
     layer) are repeated until ``min_seconds`` have elapsed; a pass is cut short at sequence
     granularity when ``max_seconds`` is reached, so the sample stays bounded for large
     workloads.  The rate is in the same GB/s units as ``value``: algorithmic bytes of the
-    sequences processed divided by the elapsed time.  BLAS is pinned to one thread, so
-    ``cores`` is 1.
+    sequences processed divided by the elapsed time.  BLAS is pinned to one thread.
     """
     import oracle
     from threadpoolctl import threadpool_limits
@@ -150,6 +157,71 @@ def cpu_baseline(w, min_seconds: float, max_seconds: float):
     }
 
 
+_POOL_STATE = {}
+
+
+def _oracle_rows(rows):
+    """Worker: the oracle's attention for some sequences of every layer (state inherited by fork)."""
+    import oracle
+
+    w, pools = _POOL_STATE["w"], _POOL_STATE["pools"]
+    for layer in range(w.layers):
+        k, v = pools[layer]
+        oracle.paged_decode_attention(w.q[layer], k, v, w.block_tables[layer], w.context_lens, 0.125, sequences=rows)
+    return len(rows), int(w.context_lens[rows].sum()) * w.layers
+
+
+def cpu_baseline_all_cores(w, min_seconds: float, max_seconds: float, max_workers: int = 16):
+    """The oracle as it stands on every host core of this process (at most ``max_workers``): the
+    append of every layer runs once in the parent (it copies the pool), then sequences are spread
+    over a fork pool with BLAS pinned to one thread per worker, in rounds until ``min_seconds``
+    (cap ``max_seconds``).  Must run before the GPU is initialised (workers are forked)."""
+    import multiprocessing as mp
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    cores = max(1, min(len(os.sched_getaffinity(0)), max_workers))
+    bytes_per_seq = (attention_bytes(w) + append_bytes(w)) / w.batch
+    chunk = 4
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        pools = [oracle.kv_append(w.k_pool, w.v_pool, w.block_tables[layer], w.positions, w.k_new[layer],
+                                  w.v_new[layer]) for layer in range(w.layers)]
+        t_append = time.perf_counter() - t0
+        _POOL_STATE.update(w=w, pools=pools)
+        seqs = tokens = 0
+        rounds = 0
+        with mp.get_context("fork").Pool(cores) as pool:
+            t1 = time.perf_counter()
+            order = [list(range(b, min(w.batch, b + chunk))) for b in range(0, w.batch, chunk)]
+            i = 0
+            while True:
+                batch = [order[(i + k) % len(order)] for k in range(cores * 2)]
+                i += len(batch)
+                for n_seq, n_tok in pool.map(_oracle_rows, batch, chunksize=1):
+                    seqs += n_seq
+                    tokens += n_tok
+                rounds += 1
+                elapsed = time.perf_counter() - t1
+                if elapsed >= min_seconds or elapsed >= max_seconds:
+                    break
+            t_attn = time.perf_counter() - t1
+        _POOL_STATE.clear()
+    secs = t_attn + t_append * seqs / w.batch  # the append is charged per pass over the batch
+    return {
+        "value": round(bytes_per_seq * seqs / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{seqs} sequence-passes of the same workload ({rounds} rounds of {cores * 2} tasks of {chunk} "
+                  f"sequences x {w.layers} layer(s)) on {cores} worker processes in {t_attn:.2f} s, plus the FP64 "
+                  f"numpy append of the whole pool once per layer ({t_append:.2f} s, charged per pass)",
+        "seconds": round(secs, 3),
+        "seq_tokens_per_s": round(tokens / secs, 1),
+    }
+
+
 # ---------------------------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------------------------
@@ -160,13 +232,20 @@ def run(args):
     import paged_kv_cache_pages_amd as pkv
     from workloads import make_config
 
-    pkv.require_library()
-    torch.cuda.set_device(0)
     t_gen = time.perf_counter()
     w = make_config(args.config)
     gen_s = time.perf_counter() - t_gen
     print(f"[bench] workload {args.config}: B={w.batch} layers={w.layers} pages={w.num_pages} "
           f"(generated in {gen_s:.1f} s)", file=sys.stderr, flush=True)
+    cpu = cpu_1 = None
+    if not args.no_cpu_baseline:  # before the GPU is touched: the all-cores leg forks workers
+        cpu = cpu_baseline_all_cores(w, args.cpu_min_seconds, args.cpu_max_seconds)
+        print(f"[bench] CPU oracle on {cpu['cores']} cores: {cpu['value']} GB/s", file=sys.stderr, flush=True)
+        cpu_1 = cpu_baseline(w, min(5.0, args.cpu_min_seconds), min(10.0, args.cpu_max_seconds))
+        print(f"[bench] CPU oracle on 1 core: {cpu_1['value']} GB/s", file=sys.stderr, flush=True)
+
+    pkv.require_library()
+    torch.cuda.set_device(0)
 
     def dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
@@ -205,6 +284,7 @@ def run(args):
                             workspace=workspace)
 
     K = args.steps
+    samples = []
 
     def timed(phases):
         """Run K steps made of ``phases`` (callables, run in order); HIP events on the launch stream
@@ -223,7 +303,9 @@ def run(args):
             ev[i][len(phases)].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return wall, [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(len(phases))]
+        per = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(len(phases))]
+        samples.append(per)
+        return wall, [float(np.mean(x)) for x in per]
 
     def graph_wall(phases):
         """The whole step captured once as a HIP graph and replayed K times: same kernels and
@@ -253,6 +335,36 @@ def run(args):
     # attention; "fused" uses pkv_decode_step, one launch per layer that also writes the new rows.
     two_wall, (append_ms, attn_ms) = timed([append_all, attend_all])
     fused_wall, (fused_ms,) = timed([fused_all])
+    attn_samples, fused_samples = samples[0][1], samples[1][0]
+
+    def stats_us(ms_list, per):
+        a = np.asarray(ms_list) * 1e3 / per
+        return {"median": round(float(np.median(a)), 3), "min": round(float(a.min()), 3),
+                "p90": round(float(np.percentile(a, 90)), 3)}
+
+    # Cold timing: before each of `reps` single steps, read a 512 MiB scratch tensor.  Reading
+    # (not writing) evicts the XCD L2s and the 256 MiB Infinity Cache without leaving dirty lines
+    # whose write-back would compete with the step.
+    evict = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    evict.sum()
+    torch.cuda.synchronize()
+
+    def cold_us(fn, reps=10):
+        times = []
+        for _ in range(reps):
+            evict.sum()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        return round(float(np.median(times)), 3)
+
+    cold_fused_us = cold_us(fused_all)
+    cold_attn_us = cold_us(attend_all)
+    del evict
     if args.graph:
         two_wall = graph_wall([append_all, attend_all])
         fused_wall = graph_wall([fused_all])
@@ -327,11 +439,19 @@ def run(args):
         "seq_tokens_per_s": round(seq_tokens(w) / (ms_per_step * 1e-3), 1),
         "bytes_per_step": step_bytes,
         "fused": {"ms_per_step": round(fused_msps, 5), "us_per_launch": round(fused_ms / w.layers * 1e3, 3),
+                  "us_per_launch_stats": stats_us(fused_samples, w.layers),
                   "value": round(gbps(step_bytes, fused_msps), 2)},
         "two_call": {"ms_per_step": round(two_ms, 5), "attention_us_per_launch": round(attn_ms / w.layers * 1e3, 3),
                      "append_us_per_step": round(append_ms * 1e3, 3), "value": round(gbps(step_bytes, two_ms), 2),
-                     "attention_gbps": round(gbps(a_bytes / w.layers, attn_ms / w.layers), 2)},
+                     "attention_gbps": round(gbps(a_bytes / w.layers, attn_ms / w.layers), 2),
+                     "attention_us_per_launch_stats": stats_us(attn_samples, w.layers)},
+        "cold": {"fused_us_per_step": cold_fused_us, "attention_us_per_step": cold_attn_us,
+                 "fused_gbps": round(gbps(step_bytes, cold_fused_us / 1e3), 2),
+                 "protocol": "median of 10 single steps, each after reading a 512 MiB scratch tensor "
+                             "(L2 and Infinity Cache evicted, no dirty lines)"},
+        "algorithmic_bytes_token_exact": attention_bytes_token_exact(w) + p_bytes,
         "copy_d2d_gbps": round(copy_gbps, 1),
+        "pct_of_copy": round(100.0 * achieved / copy_gbps, 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -348,8 +468,9 @@ def run(args):
 
     if not args.no_prefill:
         result["prefill"] = prefill_leg(args, torch, pkv)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_min_seconds, args.cpu_max_seconds)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
+        result["cpu_baseline_1core"] = cpu_1
     print(json.dumps(result), flush=True)
 
 
