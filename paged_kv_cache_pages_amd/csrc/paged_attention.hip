@@ -439,11 +439,19 @@ __global__ __launch_bounds__(64) void merge_partitions_kernel(DecodeParams p) {
   const int L = context_length<kFused>(p, b);
   const bool len_ok = L > 0 && L <= p.max_blocks * kBlock;
   const int n_pages = len_ok ? (L + kBlock - 1) / kBlock : 0;
+  // Latency, not bandwidth, bounds this kernel: every loop issues its loads (4 table entries or 8
+  // partials per lane) before using any of them, instead of one load and one wait per item.
   bool bad = false;
   const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
-  for (int i = lane; i < n_pages; i += 64) {
-    const int id = bt[i];
-    bad |= id < 0 || id >= p.num_pages;
+  for (int i0 = 0; i0 < n_pages; i0 += 256) {
+    int id[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 64 * u + lane;
+      id[u] = i < n_pages ? bt[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) bad |= id[u] < 0 || id[u] >= p.num_pages;
   }
   bad = __builtin_amdgcn_ballot_w64(bad) != 0;
   float r = 0.0f;
@@ -461,13 +469,19 @@ __global__ __launch_bounds__(64) void merge_partitions_kernel(DecodeParams p) {
     float O = 0.0f, Ls = 0.0f;
     for (int i0 = 0; i0 < n_parts; i0 += 64) {
       const int i = i0 + lane;
-      const float e = i < n_parts ? __builtin_amdgcn_exp2f(ml[2 * i] - M) : 0.0f;
+      const float e = i < n_parts ? __builtin_amdgcn_exp2f(ml[2 * i] - M) : 0.0f;  // 0 past the end
       Ls += i < n_parts ? e * ml[2 * i + 1] : 0.0f;
       const int cnt = min(64, n_parts - i0);
       const int eb = __builtin_bit_cast(int, e);
-      for (int j = 0; j < cnt; ++j) {
-        const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, j));
-        O = __builtin_fmaf(ej, po[(int64_t)(i0 + j) * kHeadDim], O);
+      for (int j0 = 0; j0 < cnt; j0 += 8) {  // j0 <= 56, so j0 + u <= 63 below
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = j0 + u < cnt ? po[(int64_t)(i0 + j0 + u) * kHeadDim] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, j0 + u));
+          O = __builtin_fmaf(ej, v[u], O);
+        }
       }
     }
     r = O / wave_sum(Ls);
