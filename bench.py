@@ -362,8 +362,8 @@ def run(args):
             times.append(e0.elapsed_time(e1) * 1e3)
         return round(float(np.median(times)), 3)
 
-    cold_fused_us = cold_us(fused_all)
-    cold_attn_us = cold_us(attend_all)
+    cold_fused_us = cold_us(fused_all) if not args.no_cold else None
+    cold_attn_us = cold_us(attend_all) if not args.no_cold else None
     del evict
     if args.graph:
         two_wall = graph_wall([append_all, attend_all])
@@ -446,7 +446,7 @@ def run(args):
                      "attention_gbps": round(gbps(a_bytes / w.layers, attn_ms / w.layers), 2),
                      "attention_us_per_launch_stats": stats_us(attn_samples, w.layers)},
         "cold": {"fused_us_per_step": cold_fused_us, "attention_us_per_step": cold_attn_us,
-                 "fused_gbps": round(gbps(step_bytes, cold_fused_us / 1e3), 2),
+                 "fused_gbps": round(gbps(step_bytes, cold_fused_us / 1e3), 2) if cold_fused_us else None,
                  "protocol": "median of 10 single steps, each after reading a 512 MiB scratch tensor "
                              "(L2 and Infinity Cache evicted, no dirty lines)"},
         "algorithmic_bytes_token_exact": attention_bytes_token_exact(w) + p_bytes,
@@ -560,6 +560,8 @@ def main():
     ap.add_argument("--step", choices=["fused", "two-call"], default="fused",
                     help="which form of the step gives value/roofline (both are timed and reported)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the paged prefill measurement")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timing (profiler runs: keeps the per-kernel averages warm)")
     ap.add_argument("--prefill-config", default="prefill16x512",
                     choices=["prefill_tiny", "prefill512", "prefill_chunked", "prefill16x512"])
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0, help="repeat CPU oracle passes at least this long")
