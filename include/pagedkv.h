@@ -201,7 +201,7 @@ pkv_status pkv_decode_step(const pkv_pool *pool, const void *q, const int32_t *b
 /*
  * Pages per partition chosen when partition_pages <= 0.  Pure function (no GPU needed):
  * no split when batch * num_kv_heads workgroups already cover the device, otherwise the
- * smallest multiple of 4 pages (at least 4) that yields about 4 workgroups per compute unit;
+ * smallest multiple of 4 pages (at least 8) that yields about 4 workgroups per compute unit;
  * never more than 256.  Returns min(max_blocks_per_seq, 256) when no split is needed; -1 on bad
  * arguments.
  */

@@ -327,8 +327,8 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   // (a merge with a path that skipped a prefetch would make it wait for a whole page instead).
   PageRegs b0, b1, b2;
   if (own_partial) load_page(b2, kbase, vbase, page_off(n_w - 1));
-  int k = 0;
   if (n_full >= 5) {
+    int k = 0;
     load_page(b0, kbase, vbase, page_off(0));
     load_page(b1, kbase, vbase, page_off(1));
     if (own_partial) process_page<true>(st, qv, with_new_token(b2), tok, tail_valid, c_log2);
@@ -340,19 +340,31 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
       load_page(b1, kbase, vbase, page_off(k + 4));
       process_page<false>(st, qv, b2, tok, kBlock, c_log2);
     }
-  } else {
-    if (n_full > 0) load_page(b0, kbase, vbase, page_off(0));
-    if (n_full > 1) load_page(b1, kbase, vbase, page_off(1));
+    // At most four full pages remain: k (in b0) and k + 1 (in b1) are already issued.
+    const int rem = n_full - k;
+    if (rem >= 3) load_page(b2, kbase, vbase, page_off(k + 2));
+    if (rem >= 1) process_page<false>(st, qv, b0, tok, kBlock, c_log2);
+    if (rem >= 4) load_page(b0, kbase, vbase, page_off(k + 3));
+    if (rem >= 2) process_page<false>(st, qv, b1, tok, kBlock, c_log2);
+    if (rem >= 3) process_page<false>(st, qv, b2, tok, kBlock, c_log2);
+    if (rem >= 4) process_page<false>(st, qv, b0, tok, kBlock, c_log2);
+  } else if (n_w > 0) {
+    // Short chain (at most four full pages): every load is issued before any page is processed,
+    // so the wave pays one memory latency, not one per buffer turn.  The four full-page loads are
+    // unconditional (slots past the wave's pages read pool page 0: table lanes past n_w hold 0;
+    // in bounds and never processed), so the issue order, and with it every wait, is the same on
+    // every path.
+    PageRegs b3, b4;
+    load_page(b0, kbase, vbase, page_off(0));
+    load_page(b1, kbase, vbase, page_off(1));
+    load_page(b3, kbase, vbase, page_off(2));
+    load_page(b4, kbase, vbase, page_off(3));
     if (own_partial) process_page<true>(st, qv, with_new_token(b2), tok, tail_valid, c_log2);
+    if (n_full >= 1) process_page<false>(st, qv, b0, tok, kBlock, c_log2);
+    if (n_full >= 2) process_page<false>(st, qv, b1, tok, kBlock, c_log2);
+    if (n_full >= 3) process_page<false>(st, qv, b3, tok, kBlock, c_log2);
+    if (n_full >= 4) process_page<false>(st, qv, b4, tok, kBlock, c_log2);
   }
-  // At most four full pages remain: k (in b0) and k + 1 (in b1) are already issued.
-  const int rem = n_full - k;
-  if (rem >= 3) load_page(b2, kbase, vbase, page_off(k + 2));
-  if (rem >= 1) process_page<false>(st, qv, b0, tok, kBlock, c_log2);
-  if (rem >= 4) load_page(b0, kbase, vbase, page_off(k + 3));
-  if (rem >= 2) process_page<false>(st, qv, b1, tok, kBlock, c_log2);
-  if (rem >= 3) process_page<false>(st, qv, b2, tok, kBlock, c_log2);
-  if (rem >= 4) process_page<false>(st, qv, b0, tok, kBlock, c_log2);
 
   // Wavefront -> LDS.  Fold token t and t+1 (the two halves of each 16-lane row) first.
 #pragma unroll

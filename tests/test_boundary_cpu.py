@@ -48,13 +48,13 @@ def test_status_strings_and_version(lib):
 def test_partition_planning():
     plan = lambda b, h, t, c: pkv.plan_partition_pages(b, h, t, num_cus=c)
     assert plan(256, 8, 128, 256) == 128  # 2048 (sequence, head) workgroups: no split
-    assert plan(1, 8, 128, 256) == 4  # one long sequence: 32 partitions of 4 pages
+    assert plan(1, 8, 128, 256) == 8  # one long sequence: 16 partitions of 8 pages (the minimum)
     assert plan(16, 8, 128, 256) == 16
     assert plan(17, 8, 128, 256) == 20
     assert plan(64, 8, 128, 256) == 128
     for b in range(0, 300, 7):
         p = plan(b, 8, 128, 256)
-        assert 4 <= p <= 128 and (p == 128 or p % 4 == 0)
+        assert 8 <= p <= 128 and (p == 128 or p % 4 == 0)
     assert pkv.library().pkv_plan_partition_pages(-1, 8, 128, 256) == -1
 
 
