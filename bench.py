@@ -402,6 +402,36 @@ def run(args):
         kernel = "paged_decode_kernel"
     if pp < w.max_blocks:
         kernel += " + merge_partitions_kernel"
+
+    def graph_launch_ms(phase, reps):
+        """Mean ms per step of `reps` steps of `phase` captured in one HIP graph and replayed between
+        two events on the launch stream: the GPU never waits for the host, so this is the kernels'
+        own duration plus the gaps between graph nodes."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            phase()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(reps):
+                phase()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del graph
+        return e0.elapsed_time(e1) / reps
+
+    # The roofline uses the mean of the per-launch events.  Back-to-back launches replayed from one
+    # graph are reported beside it: they remove host launch gaps (which matter for short kernels)
+    # but add the graph's node-to-node gap (bw256: 171.7 vs 168.4 us, rocprof 166.2 us).
+    reps = max(10, min(K, 100))
+    launch_ms_graph = graph_launch_ms(fused_all if fused_mode else attend_all, reps) / w.layers
     achieved = gbps(launch_bytes, launch_ms)
     traffic = recorded_traffic("fused" if fused_mode else "attention") \
         if pp >= w.max_blocks and args.config == "bw256" else None
@@ -461,6 +491,9 @@ def run(args):
             "traffic": traffic,
             "kernel": kernel,
             "algorithmic_bytes_per_launch": launch_bytes,
+            "us_per_launch": round(launch_ms * 1e3, 3),
+            "timing": "mean of HIP events around each launch, on the launch stream",
+            "us_per_launch_graph": round(launch_ms_graph * 1e3, 3),
         },
         "note": "The reference pages report no throughput or hardware numbers for this kernel; "
                 "figures are this build's measurements on one MI355X.",
