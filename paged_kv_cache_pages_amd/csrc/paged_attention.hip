@@ -218,8 +218,13 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int part = blockIdx.x % p.num_parts;
-  const int pair = blockIdx.x / p.num_parts;
+  // Partition-major order: consecutive workgroup ids go to the 8 XCDs in turn, so with the
+  // partition as the fast index (and 8 partitions) partition k would always land on XCD k, and the
+  // XCD holding every sequence's first partition would do most of the work.  With the (sequence,
+  // KV head) pair fast, each partition is spread over all XCDs.
+  const int pairs = p.batch * p.num_kv_heads;
+  const int part = blockIdx.x / pairs;
+  const int pair = blockIdx.x % pairs;
   const int g = pair % p.num_kv_heads;
   const int b = pair / p.num_kv_heads;
   const int qh0 = g * kGroup;  // first query head of the group
