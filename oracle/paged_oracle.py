@@ -20,6 +20,10 @@ What it computes, in the plainest reading of the pages:
 
 Pool layout: ``[page][kv_head][token_in_page][dim]`` for K and V separately.
 
+Out-of-range inputs (the pages assume none) follow the library's error rule: an append row whose
+position lies outside the table's span or whose entry names no page of the pool is not written,
+and a sequence whose context does not map to pages of the pool gets an all-zero output.
+
 Every oracle function is pinned by ``tests/test_oracle_pins.py`` against closed forms, an
 independent brute-force implementation, invariants and ``torch`` scaled-dot-product attention.
 """
@@ -77,6 +81,26 @@ def locate_slot(block_table_row: np.ndarray, pos: int) -> tuple[int, int]:
     return int(block_table_row[pos // BLOCK_SIZE]), pos % BLOCK_SIZE
 
 
+# The pages assume valid inputs.  For the rest this oracle follows the library's error rule: a row
+# whose position lies outside the table's span, or whose table entry names no page of the pool, is
+# not written; a sequence whose context cannot be read that way gets an all-zero output.  (Python's
+# negative indexing would otherwise turn position -1 or entry -1 into the last slot or page.)
+
+def slot_in_pool(block_table_row: np.ndarray, pos: int, num_pages: int) -> bool:
+    """Whether position ``pos`` maps through the row to a slot of a pool of ``num_pages`` pages."""
+    if pos < 0 or pos >= len(block_table_row) * BLOCK_SIZE:
+        return False
+    return 0 <= int(block_table_row[pos // BLOCK_SIZE]) < num_pages
+
+
+def context_in_pool(block_table_row: np.ndarray, length: int, num_pages: int) -> bool:
+    """Whether positions ``0 .. length - 1`` all map to slots of the pool (``length`` 0 is valid)."""
+    if length < 0 or length > len(block_table_row) * BLOCK_SIZE:
+        return False
+    entries = np.asarray(block_table_row[:(length + BLOCK_SIZE - 1) // BLOCK_SIZE], dtype=np.int64)
+    return bool(np.all((entries >= 0) & (entries < num_pages)))
+
+
 def kv_append(k_pool, v_pool, block_tables, positions, k_new, v_new):
     """Return copies of the pools with every sequence's new K/V row written at its position.
 
@@ -86,6 +110,8 @@ def kv_append(k_pool, v_pool, block_tables, positions, k_new, v_new):
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
     for b in range(len(positions)):
+        if not slot_in_pool(block_tables[b], int(positions[b]), k_out.shape[0]):
+            continue  # skipped, not written
         page, slot = locate_slot(block_tables[b], int(positions[b]))
         k_out[page, :, slot, :] = k_new[b]
         v_out[page, :, slot, :] = v_new[b]
@@ -131,7 +157,8 @@ def attend_one(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float
 
 
 def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale=0.125, sequences=None):
-    """FP64 attention output [B][Hq][D] for a decode batch (context 0 gives zeros).
+    """FP64 attention output [B][Hq][D] for a decode batch (context 0, or a context that does not
+    map to pages of the pool, gives zeros).
 
     ``q``: uint16 [B][Hq][D]; pools uint16 [P][Hkv][16][D]; ``block_tables`` int32 [B][T];
     ``context_lens`` [B] counts the appended token.  ``sequences`` optionally restricts the work to
@@ -143,7 +170,7 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale=
     rows = range(batch) if sequences is None else sequences
     for b in rows:
         L = int(context_lens[b])
-        if L == 0:
+        if L == 0 or not context_in_pool(block_tables[b], L, k_pool.shape[0]):
             out[b] = 0.0
             continue
         keys = bf16_bits_to_f64(gather_context(k_pool, block_tables[b], L))

@@ -19,6 +19,9 @@ Readings: the article rounds the score and probability matrices to BF16 between 
 oracle is the exact definition in FP64 with no intermediate rounding (the same target the
 decode path is held to).  ``start > 0`` generalises the article's whole-prompt prefill to a prompt
 chunk behind ``start`` cached tokens: query row ``i`` attends to positions ``0 .. start + i``.
+Out-of-range inputs follow the library's error rule: a prompt with a negative start writes
+nothing, a row whose position has no page of the pool is not written, and every output row of a
+prompt whose positions ``0 .. start + n - 1`` do not all map to pages of the pool is zero.
 
 Pinned by ``tests/test_oracle_prefill_pins.py``.
 """
@@ -27,7 +30,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .paged_oracle import BLOCK_SIZE, bf16_bits_to_f64, gather_context, kv_head_of, locate_slot
+from .paged_oracle import (BLOCK_SIZE, bf16_bits_to_f64, context_in_pool, gather_context, kv_head_of, locate_slot,
+                           slot_in_pool)
 
 
 def prefill_kv_append(k_pool, v_pool, block_tables, cu_seqlens, start_pos, k_new, v_new):
@@ -39,8 +43,12 @@ def prefill_kv_append(k_pool, v_pool, block_tables, cu_seqlens, start_pos, k_new
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
     for b in range(len(start_pos)):
+        if int(start_pos[b]) < 0:
+            continue  # the whole prompt is skipped
         for row in range(int(cu_seqlens[b]), int(cu_seqlens[b + 1])):
             pos = int(start_pos[b]) + row - int(cu_seqlens[b])
+            if not slot_in_pool(block_tables[b], pos, k_out.shape[0]):
+                continue  # this row is skipped
             page, slot = locate_slot(block_tables[b], pos)
             k_out[page, :, slot, :] = k_new[row]
             v_out[page, :, slot, :] = v_new[row]
@@ -83,6 +91,9 @@ def paged_prefill_attention(q, k_pool, v_pool, block_tables, cu_seqlens, start_p
         if not sel:
             continue
         start = int(start_pos[b])
+        if start < 0 or not context_in_pool(block_tables[b], start + hi - lo, k_pool.shape[0]):
+            out[sel] = 0.0  # the whole prompt cannot be read through its table
+            continue
         positions = np.array([start + r - lo for r in sel])
         L = int(positions.max()) + 1
         keys = bf16_bits_to_f64(gather_context(k_pool, block_tables[b], L))

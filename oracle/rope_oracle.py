@@ -19,14 +19,16 @@ match it exactly.  Queries and keys are rotated; values are not.
 
 The decode step rotates each sequence's query heads and its new key row at the sequence's absolute
 position and then appends the rotated key and the unrotated value exactly like
-``paged_oracle.kv_append``.
+``paged_oracle.kv_append``.  A sequence whose position has no row in the tables or no slot in the
+pool is skipped entirely (the library's error rule): its q rows come back unchanged and nothing
+is written to the pool.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .paged_oracle import bf16_round_nearest_even, kv_append
+from .paged_oracle import bf16_round_nearest_even, kv_append, slot_in_pool
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -63,8 +65,13 @@ def rope_kv_append(k_pool, v_pool, block_tables, positions, q, k_new, v_new, cos
     """
     q_out = np.array(q, copy=True)
     k_rot = np.array(k_new, copy=True)
+    used = np.array(positions, dtype=np.int64, copy=True)
     for b, pos in enumerate(np.asarray(positions)):
-        q_out[b] = rope_rotate(q[b], int(pos), cos_table, sin_table)
-        k_rot[b] = rope_rotate(k_new[b], int(pos), cos_table, sin_table)
-    k_out, v_out = kv_append(k_pool, v_pool, block_tables, positions, k_rot, v_new)
+        pos = int(pos)
+        if not (0 <= pos < len(cos_table)) or not slot_in_pool(block_tables[b], pos, np.shape(k_pool)[0]):
+            used[b] = -1  # the whole sequence is skipped: q_out keeps q, the pool is not written
+            continue
+        q_out[b] = rope_rotate(q[b], pos, cos_table, sin_table)
+        k_rot[b] = rope_rotate(k_new[b], pos, cos_table, sin_table)
+    k_out, v_out = kv_append(k_pool, v_pool, block_tables, used, k_rot, v_new)
     return q_out, k_out, v_out

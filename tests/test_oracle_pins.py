@@ -323,6 +323,35 @@ def check_bf16_rounding():
     assert np.array_equal(oracle.bf16_round_nearest_even(x), ref)
 
 
+def check_out_of_range():
+    """O14: rows and contexts outside the table or the pool follow the library's error rule
+    (append: not written; attention: an all-zero row), never Python's wrap-around indexing."""
+    rng = np.random.default_rng(114)
+    P = 6
+    k_pool = normal_bf16(rng, (P, 2, 16, 64))
+    v_pool = normal_bf16(rng, (P, 2, 16, 64))
+    # table span = 2 pages = 32 positions
+    tables = np.array([[3, 1], [2, 4], [-1, 0], [2, -1], [P, 1], [5, 0]], dtype=np.int32)
+    positions = np.array([5, -1, 3, 20, 7, 32])  # only row 0 names a slot of the pool
+    k_new = normal_bf16(rng, (6, 2, 64))
+    v_new = normal_bf16(rng, (6, 2, 64))
+    k2, v2 = oracle.kv_append(k_pool, v_pool, tables, positions, k_new, v_new)
+    k_ref, v_ref = k_pool.copy(), v_pool.copy()
+    k_ref[3, :, 5, :] = k_new[0]
+    v_ref[3, :, 5, :] = v_new[0]
+    assert np.array_equal(k2, k_ref) and np.array_equal(v2, v_ref)
+    # attention: context 16 with a bad second entry is valid (only page 0 is read); the others
+    # ask for a page that is not in the pool or for more than the table spans
+    q = normal_bf16(rng, (6, 8, 64))
+    tables = np.array([[3, -1], [3, 1], [-1, 2], [3, P], [3, 1], [3, 1]], dtype=np.int32)
+    lens = np.array([16, 33, 4, 17, -1, 0])
+    out = oracle.paged_decode_attention(q, k_pool, v_pool, tables, lens)
+    assert np.array_equal(out[1:], np.zeros_like(out[1:]))
+    k_rows = k_pool[3].transpose(1, 0, 2)  # [16][Hkv][D] of page 3
+    v_rows = v_pool[3].transpose(1, 0, 2)
+    assert np.max(np.abs(out[0] - brute_force(q[0], k_rows, v_rows, 0.125))) <= 1e-12
+
+
 PINS = {
     "brute_force": check_brute_force,
     "single_token": check_single_token,
@@ -338,6 +367,7 @@ PINS = {
     "append_then_attend_single": check_append_then_attend_single,
     "torch_sdpa": check_torch_sdpa,
     "bf16_rounding": check_bf16_rounding,
+    "out_of_range": check_out_of_range,
 }
 
 
@@ -386,6 +416,8 @@ MUTATIONS = {
                                   ["softmax_rows", "two_tokens"]),
     "slot_swapped": ("locate_slot", lambda row, pos: (int(row[pos % 16]), pos // 16), ["append"]),
     "merge_wrong_sign": ("merge_states", _merge_wrong_sign, ["online_equals_two_pass"]),
+    "append_unchecked": ("slot_in_pool", lambda row, pos, n: True, ["out_of_range"]),
+    "attention_unchecked": ("context_in_pool", lambda row, length, n: True, ["out_of_range"]),
     "bf16_decode_shift": ("bf16_bits_to_f64",
                           lambda b: (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64),
                           ["single_token"]),

@@ -170,7 +170,40 @@ def test_gqa_mapping_with_constant_values_per_kv_head():
         assert np.allclose(out[:, h, :], expect, rtol=0, atol=1e-15)
 
 
-@pytest.mark.parametrize("mistake", ["mask_off_by_one", "wrong_kv_head", "no_scale", "append_shift"])
+def test_out_of_range_prompts_follow_the_error_rule():
+    """A negative start writes nothing; a row whose position has no page of the pool is not
+    written while the prompt's other rows are; a prompt that cannot be read through its table
+    gets all-zero rows; a valid prompt in the same batch is unaffected."""
+    w = make_prefill(3, [5, 6, 4, 3], [0, 0, 0, 0], max_blocks=2)
+    w.start_pos[:] = [0, -2, 14, 30]  # prompt 2 crosses into block 1, prompt 3 runs past the span
+    P = w.k_pool.shape[0]
+    spare = sorted(set(range(P)) - set(int(x) for x in w.block_tables.ravel() if x >= 0))
+    w.block_tables[2, 1] = -1  # prompt 2's second page is missing
+    w.block_tables[3, 1] = spare[0]  # prompt 3's positions 30, 31 have a page; 32 is past the span
+    kp = np.full_like(w.k_pool, 0x7FC0)
+    vp = np.full_like(w.v_pool, 0x7FC0)
+    k2, v2 = oracle.prefill_kv_append(kp, vp, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, w.v_new)
+    expect_k, expect_v = kp.copy(), vp.copy()
+    def put(b, i):
+        pos = int(w.start_pos[b]) + i
+        page, slot = int(w.block_tables[b, pos // 16]), pos % 16
+        row = int(w.cu_seqlens[b]) + i
+        expect_k[page, :, slot] = w.k_new[row]
+        expect_v[page, :, slot] = w.v_new[row]
+    for i in range(5):
+        put(0, i)  # valid prompt: every row
+    put(2, 0), put(2, 1)  # positions 14, 15 have a page; 16, 17 do not
+    put(3, 0), put(3, 1)  # positions 30, 31 are inside the span; 32 is not
+    assert np.array_equal(k2, expect_k) and np.array_equal(v2, expect_v)
+    out = oracle.paged_prefill_attention(w.q, k2, v2, w.block_tables, w.cu_seqlens, w.start_pos)
+    lo = int(w.cu_seqlens[1])
+    assert np.array_equal(out[lo:], np.zeros_like(out[lo:]))
+    first = oracle.paged_prefill_attention(w.q, k2, v2, w.block_tables[:1], w.cu_seqlens[:2], w.start_pos[:1])
+    assert np.array_equal(out[:lo], first[:lo]) and np.all(np.isfinite(out[:lo])) and np.any(out[:lo] != 0)
+
+
+@pytest.mark.parametrize("mistake", ["mask_off_by_one", "wrong_kv_head", "no_scale", "append_shift", "append_unchecked",
+                                     "attention_unchecked"])
 def test_planted_mistakes_are_caught(monkeypatch, mistake):
     """Each plausible mistake, planted in the oracle, fails one of the pins above."""
     import oracle.prefill_oracle as po
@@ -190,6 +223,14 @@ def test_planted_mistakes_are_caught(monkeypatch, mistake):
         monkeypatch.setattr(po, "causal_attention_rows", lambda q, k, v, s, scale: real(q, k, v, s, 1.0))
         with pytest.raises(AssertionError):
             test_brute_force_rows()
+    elif mistake == "append_unchecked":
+        monkeypatch.setattr(po, "slot_in_pool", lambda row, pos, n: True)
+        with pytest.raises((AssertionError, IndexError, ValueError)):
+            test_out_of_range_prompts_follow_the_error_rule()
+    elif mistake == "attention_unchecked":
+        monkeypatch.setattr(po, "context_in_pool", lambda row, length, n: True)
+        with pytest.raises((AssertionError, IndexError, ValueError)):
+            test_out_of_range_prompts_follow_the_error_rule()
     elif mistake == "append_shift":
         real = po.locate_slot
         monkeypatch.setattr(po, "locate_slot", lambda row, pos: real(row, pos + 1))

@@ -163,6 +163,29 @@ def check_rope_append():
     assert len(changed) <= w.batch * w.num_kv_heads
 
 
+def check_out_of_range_skipped():
+    """A sequence whose position has no table row, lies outside the block table, or maps to no
+    page of the pool is skipped entirely: its q rows come back unchanged and the pool is not
+    written; the valid sequence in the same batch is rotated and appended."""
+    rng = np.random.default_rng(316)
+    P = 4
+    k_pool = normal_bf16(rng, (P, 2, 16, 64))
+    v_pool = normal_bf16(rng, (P, 2, 16, 64))
+    q = normal_bf16(rng, (5, 8, 64))
+    k_new = normal_bf16(rng, (5, 2, 64))
+    v_new = normal_bf16(rng, (5, 2, 64))
+    cos, sin = angle_tables(np.linspace(0.1, 1.0, 32), rows=20)
+    tables = np.array([[1, 2], [1, 2], [1, 2], [-1, 2], [P, 2]], dtype=np.int32)
+    positions = np.array([3, -1, 20, 5, 6])  # rows 20.. are past the tables (20 rows)
+    q2, k2, v2 = oracle.rope_kv_append(k_pool, v_pool, tables, positions, q, k_new, v_new, cos, sin)
+    assert np.array_equal(q2[1:], q[1:])
+    k_ref, v_ref = k_pool.copy(), v_pool.copy()
+    k_ref[1, :, 3] = oracle.rope_rotate(k_new[0], 3, cos, sin)
+    v_ref[1, :, 3] = v_new[0]
+    assert np.array_equal(k2, k_ref) and np.array_equal(v2, v_ref)
+    assert np.array_equal(q2[0], oracle.rope_rotate(q[0], 3, cos, sin)) and not np.array_equal(q2[0], q[0])
+
+
 PINS = {
     "position_zero_identity": check_position_zero_identity,
     "quarter_and_half_turns": check_quarter_and_half_turns,
@@ -173,6 +196,7 @@ PINS = {
     "fp32_rounding_order": check_fp32_rounding_order,
     "rounding_order_tie": check_rounding_order_tie,
     "rope_append": check_rope_append,
+    "out_of_range_skipped": check_out_of_range_skipped,
 }
 
 
