@@ -254,6 +254,43 @@ def test_append_skips_out_of_range_rows(gpu):
     assert np.array_equal(bf16_to_bits(d["v_pool"]), w.v_pool)
 
 
+def test_out_of_range_rows_match_the_oracle(gpu):
+    """A batch mixing valid rows with every kind of out-of-range row (negative position, position
+    past the table, entry -1, entry past the pool, empty sequence): the append, the attention on
+    both paths and the fused step all equal the oracle, which skips such rows and zeroes such
+    sequences."""
+    import torch
+
+    w = make_custom(seed=33, lengths=[10, 20, 30, 0, 40, 50, 17])
+    pos = w.positions.copy()
+    bt = w.block_tables[0].copy()
+    pos[1] = -5
+    pos[2] = 128 * 16
+    bt[4, 2] = -1  # position 39 -> block 2 unassigned
+    bt[5, 3] = w.num_pages  # position 49 -> block 3 past the pool
+    lens = np.where(pos >= 0, pos + 1, 0)
+    lens[2] = 128 * 16 + 1  # past the table's span
+    print(f"[out of range] positions={pos.tolist()} lens={lens.tolist()}", flush=True)
+    rk, rv = oracle.kv_append(w.k_pool, w.v_pool, bt, pos, w.k_new[0], w.v_new[0])
+    ref = oracle.paged_decode_attention(w.q[0], rk, rv, bt, lens)
+    assert np.all(ref[[1, 2, 3, 4, 5]] == 0) and np.all(ref[[0, 6]] != 0)
+    d = upload(w)
+    gpu.kv_append(d["k_pool"], d["v_pool"], to_gpu_i32(bt), to_gpu_i32(pos), d["k_new"], d["v_new"])
+    outs = [attend(gpu, d["q"], d["k_pool"], d["v_pool"], to_gpu_i32(bt), to_gpu_i32(lens), partition_pages=pp)
+            for pp in (4, 128)]
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_bits(d["k_pool"]), rk) and np.array_equal(bf16_to_bits(d["v_pool"]), rv)
+    for pp, out in zip((4, 128), outs):
+        assert_close(out.cpu().numpy(), ref, f"out of range pp={pp}")
+    f = upload(w)
+    fused = gpu.decode_step(f["q"], f["k_pool"], f["v_pool"], to_gpu_i32(bt), to_gpu_i32(pos), f["k_new"], f["v_new"],
+                            out_dtype=torch.float32, partition_pages=4)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_bits(f["k_pool"]), rk) and np.array_equal(bf16_to_bits(f["v_pool"]), rv)
+    # the fused step attends over positions + 1 tokens: the same contexts as `lens`
+    assert_close(fused.cpu().numpy(), ref, "fused out of range")
+
+
 def test_debug_validation_rejects_bad_data(gpu):
     import torch
 
