@@ -188,8 +188,10 @@ pkv_status pkv_paged_decode_attention(const void *q, const void *k_pool, const v
  *   pool, block_tables, positions, k_new, v_new   as for pkv_kv_append
  *   q, out, out_dtype, scale, partition_pages, workspace   as for pkv_paged_decode_attention
  *   num_q_heads                                   4 * pool->num_kv_heads
- * A position outside [0, 16 * max_blocks_per_seq) or a needed table entry outside [0, num_pages)
- * appends nothing and zeroes that sequence's output rows, as the two separate calls would.
+ * Out-of-range data behaves exactly as with the two separate calls: a position outside
+ * [0, 16 * max_blocks_per_seq), or an append page entry outside [0, num_pages), appends nothing;
+ * any needed table entry outside [0, num_pages) zeroes that sequence's output rows (the row is
+ * still appended when its own page entry is valid).
  * Precondition (as for the separate calls): no other sequence of the batch references the page
  * a sequence appends to.
  */

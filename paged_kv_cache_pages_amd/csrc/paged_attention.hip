@@ -265,11 +265,16 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   // One table entry per lane, range-checked before any page is touched.
   const int ids = lane < n_w ? bt[(int64_t)kWaves * lane] : 0;
   const bool bad = __builtin_amdgcn_ballot_w64(ids < 0 || ids >= p.num_pages) != 0;
-  if (bad) n_w = 0;
   // The wavefront holding the sequence's last page (it always holds the new token).
-  const bool owns_last = n_w > 0 && p1 == n_pages && p0 + wave + kWaves * (n_w - 1) == n_pages - 1;
+  const bool holds_last = n_w > 0 && p1 == n_pages && p0 + wave + kWaves * (n_w - 1) == n_pages - 1;
+  // Like pkv_kv_append, the fused append depends only on its own page entry: an invalid entry
+  // elsewhere in the sequence zeroes the output but does not stop the append.
+  const int last_id = holds_last ? __builtin_amdgcn_readlane(ids, n_w - 1) : -1;
+  const bool do_append = kFused && last_id >= 0 && last_id < p.num_pages;
+  if (bad) n_w = 0;
+  const bool owns_last = n_w > 0 && holds_last;
   uint4 knew = make_uint4(0u, 0u, 0u, 0u), vnew = knew;
-  if (kFused && owns_last) {
+  if (do_append) {
     const int64_t row = ((int64_t)b * p.num_kv_heads + g) * kHeadDim + chunk * 8;
     knew = load16(p.k_new + row);
     vnew = load16(p.v_new + row);
@@ -302,14 +307,13 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   const int tail_valid = L - (n_pages - 1) * kBlock;
   const bool own_partial = owns_last;
   const int n_full = own_partial ? n_w - 1 : n_w;
-  if (kFused && own_partial) {
+  if (do_append) {
     // Append: the 8 lanes that hold the new token's slot write its K and V rows (16 B each) into
     // the pool.  The same rows replace that slot in registers below, so the attention never
     // depends on when these stores become visible.
     const int slot = tail_valid - 1;  // position % 16
     if (tok == (slot & 7)) {
-      const int64_t dst = ((int64_t)__builtin_amdgcn_readlane(ids, n_w - 1) * p.num_kv_heads + g) * (kBlock * kHeadDim) +
-                          slot * kHeadDim + chunk * 8;
+      const int64_t dst = ((int64_t)last_id * p.num_kv_heads + g) * (kBlock * kHeadDim) + slot * kHeadDim + chunk * 8;
       *reinterpret_cast<uint4 *>(p.k_pool_w + dst) = knew;
       *reinterpret_cast<uint4 *>(p.v_pool_w + dst) = vnew;
     }
@@ -416,11 +420,13 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   }
 
   if (kSplit) {
+    // A partition that met an invalid table entry marks its slot with a negative denominator (a
+    // real one is positive), so the merge zeroes the sequence without reading the table again.
     const int64_t slot = ((int64_t)b * p.num_q_heads + qh0 + h) * p.num_parts + part;
     p.part_o[slot * kHeadDim + d] = O;
     if (d == 0) {
       p.part_ml[slot * 2 + 0] = M;
-      p.part_ml[slot * 2 + 1] = Ls;
+      p.part_ml[slot * 2 + 1] = any_bad ? -1.0f : Ls;
     }
   } else {
     const float r = any_bad ? 0.0f : O / Ls;
@@ -432,10 +438,9 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
 
 // Combine the partitions of one (sequence, query head): M = max m_i, O = sum o_i 2^(m_i - M),
 // l = sum l_i 2^(m_i - M), out = O / l.  One wavefront: the partitions' (m, l) pairs are spread
-// over the lanes (64 at a time) for the max and the weighted sum; then lane d accumulates dim d of
-// the partial outputs with the weights broadcast from the lanes that hold them.  The sequence's
-// table row is re-validated here, so an invalid entry anywhere zeroes the row exactly as the
-// unsplit kernel does.
+// over the lanes for the max and the weighted sum; lane d accumulates dim d of the partial outputs
+// with the weights broadcast from the lanes that hold them.  A slot marked invalid by its
+// partition (negative l) zeroes the sequence, as the unsplit kernel does.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmax_plain(x, __shfl_xor(x, o));
@@ -448,60 +453,82 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Partitions whose partial outputs the merge holds in registers at once.
+constexpr int kMergeRegParts = 16;
+
 template <bool kOutBf16, bool kFused>
 __global__ __launch_bounds__(64) void merge_partitions_kernel(DecodeParams p) {
   const int b = blockIdx.x / p.num_q_heads;
   const int h = blockIdx.x % p.num_q_heads;
   const int lane = threadIdx.x;
+  const int64_t slot0 = ((int64_t)b * p.num_q_heads + h) * p.num_parts;
+  const float *ml = p.part_ml + slot0 * 2;
+  const float *po = p.part_o + slot0 * kHeadDim + lane;
+
+  // The kernel is latency-bound: the (m, l) pairs of the first 64 slots and the partial outputs of
+  // the first kMergeRegParts slots are loaded together with the context length, in one round trip.
+  // Slot indexes are clamped to the launch's partition count, so every load is in bounds; slots
+  // past the sequence's own partitions hold stale data and are discarded by index below.
+  const int last = p.num_parts - 1;
+  const float2 mlv = *reinterpret_cast<const float2 *>(ml + 2 * min(lane, last));
+  float v[kMergeRegParts];
+#pragma unroll
+  for (int u = 0; u < kMergeRegParts; ++u) v[u] = po[(int64_t)min(u, last) * kHeadDim];
+  // Keep the scheduler from placing these loads after the wait for the context length.
+  __builtin_amdgcn_sched_barrier(0);
+
   const int L = context_length<kFused>(p, b);
   const bool len_ok = L > 0 && L <= p.max_blocks * kBlock;
   const int n_pages = len_ok ? (L + kBlock - 1) / kBlock : 0;
-  // Latency, not bandwidth, bounds this kernel: every loop issues its loads (4 table entries or 8
-  // partials per lane) before using any of them, instead of one load and one wait per item.
-  bool bad = false;
-  const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
-  for (int i0 = 0; i0 < n_pages; i0 += 256) {
-    int id[4];
+  const int n_parts = (n_pages + p.part_pages - 1) / p.part_pages;  // <= num_parts
+  // Up to kMergeRegParts partitions, straight from the registers.  This runs unconditionally (the
+  // masks make it harmless otherwise) so the compiler keeps the loads above ahead of every branch.
+  const bool mine = lane < n_parts;
+  const float m = mine ? mlv.x : -INFINITY;
+  const float l = mine ? mlv.y : 0.0f;
+  const bool bad = __builtin_amdgcn_ballot_w64(mine && !(l >= 0.0f)) != 0;
+  const float M = wave_max(m);
+  const float e = mine ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+  const float Ls = wave_sum(e * l);
+  const int eb = __builtin_bit_cast(int, e);
+  float O = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + 64 * u + lane;
-      id[u] = i < n_pages ? bt[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) bad |= id[u] < 0 || id[u] >= p.num_pages;
-  }
-  bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-  float r = 0.0f;
-  if (len_ok && !bad) {
-    const int n_parts = (n_pages + p.part_pages - 1) / p.part_pages;
-    const int64_t slot0 = ((int64_t)b * p.num_q_heads + h) * p.num_parts;
-    const float *ml = p.part_ml + slot0 * 2;
-    const float *po = p.part_o + slot0 * kHeadDim + lane;
-    float M = -INFINITY;
+  for (int u = 0; u < kMergeRegParts; ++u)
+    if (u < n_parts) O = __builtin_fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, u)), v[u], O);
+  float r = (n_parts > 0 && n_parts <= kMergeRegParts && !bad) ? O / Ls : 0.0f;
+  if (n_parts > kMergeRegParts) {
+    // Long splits: the pairs 64 at a time, the partial outputs 8 at a time per lane.
+    bool any_bad = false;
+    float Mg = -INFINITY;
     for (int i0 = 0; i0 < n_parts; i0 += 64) {
       const int i = i0 + lane;
-      M = fmax_plain(M, i < n_parts ? ml[2 * i] : -INFINITY);
-    }
-    M = wave_max(M);
-    float O = 0.0f, Ls = 0.0f;
-    for (int i0 = 0; i0 < n_parts; i0 += 64) {
-      const int i = i0 + lane;
-      const float e = i < n_parts ? __builtin_amdgcn_exp2f(ml[2 * i] - M) : 0.0f;  // 0 past the end
-      Ls += i < n_parts ? e * ml[2 * i + 1] : 0.0f;
-      const int cnt = min(64, n_parts - i0);
-      const int eb = __builtin_bit_cast(int, e);
-      for (int j0 = 0; j0 < cnt; j0 += 8) {  // j0 <= 56, so j0 + u <= 63 below
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = j0 + u < cnt ? po[(int64_t)(i0 + j0 + u) * kHeadDim] : 0.0f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, j0 + u));
-          O = __builtin_fmaf(ej, v[u], O);
-        }
+      if (i < n_parts) {
+        Mg = fmax_plain(Mg, ml[2 * i]);
+        any_bad |= !(ml[2 * i + 1] >= 0.0f);
       }
     }
-    r = O / wave_sum(Ls);
+    if (__builtin_amdgcn_ballot_w64(any_bad) == 0) {
+      Mg = wave_max(Mg);
+      float Og = 0.0f, Lg = 0.0f;
+      for (int i0 = 0; i0 < n_parts; i0 += 64) {
+        const int i = i0 + lane;
+        const float ei = i < n_parts ? __builtin_amdgcn_exp2f(ml[2 * i] - Mg) : 0.0f;  // 0 past the end
+        Lg += i < n_parts ? ei * ml[2 * i + 1] : 0.0f;
+        const int cnt = min(64, n_parts - i0);
+        const int eib = __builtin_bit_cast(int, ei);
+        for (int j0 = 0; j0 < cnt; j0 += 8) {  // j0 <= 56, so j0 + u <= 63 below
+          float w[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) w[u] = j0 + u < cnt ? po[(int64_t)(i0 + j0 + u) * kHeadDim] : 0.0f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eib, j0 + u));
+            Og = __builtin_fmaf(ej, w[u], Og);
+          }
+        }
+      }
+      r = Og / wave_sum(Lg);
+    }
   }
   const int64_t o = ((int64_t)b * p.num_q_heads + h) * kHeadDim + lane;
   if (kOutBf16) static_cast<uint16_t *>(p.out)[o] = f32_to_bf16_rne(r);

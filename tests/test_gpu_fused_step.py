@@ -97,13 +97,16 @@ def test_fused_step_invalid_rows(gpu, partition_pages):
     exactly as with the two separate calls."""
     import torch
 
-    w = make_custom(seed=71, lengths=[40, 70, 20, 90, 33])
+    w = make_custom(seed=71, lengths=[40, 70, 20, 90, 33, 137])
     pos = w.positions.copy()
     pos[0] = -1
     pos[2] = 128 * 16
     bt = w.block_tables[0].copy()
     bt[3, 5] = -7  # position 89 -> block 5
     bt[4, 0] = w.num_pages  # a context page (not the append page) out of range
+    # block 4 shares a wavefront with the append page (block 8) when both are in one partition:
+    # the row is still appended, as pkv_kv_append does, and the output row is zero
+    bt[5, 4] = -3
     d = upload(w)
     k1, v1 = d["k_pool"], d["v_pool"]
     k2, v2 = k1.clone(), v1.clone()
@@ -114,9 +117,11 @@ def test_fused_step_invalid_rows(gpu, partition_pages):
     assert torch.equal(a, b)
     assert torch.equal(k1, k2) and torch.equal(v1, v2)
     got = b.cpu().numpy()
-    for row in (0, 2, 3, 4):
+    for row in (0, 2, 3, 4, 5):
         assert np.all(got[row] == 0), row
     assert np.any(got[1] != 0)
+    page = int(bt[5, 8])
+    assert np.array_equal(bf16_to_bits(k2)[page, :, 136 % 16], w.k_new[0, 5])
 
 
 def test_fused_step_debug_validation(gpu):
