@@ -264,8 +264,9 @@ def run(args):
             "v_new": dev_bf16(w.v_new[layer]),
             "out": torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda"),
         })
+    # The scheduler knows every context length on the host, so the plan gets the longest one.
     pp = args.partition_pages if args.partition_pages > 0 else pkv.plan_partition_pages(
-        w.batch, w.num_kv_heads, w.max_blocks)
+        w.batch, w.num_kv_heads, w.max_blocks, max_context=int(np.max(w.context_lens)) if w.batch else None)
     ws_bytes = pkv.decode_workspace_bytes(w.batch, w.num_q_heads, w.max_blocks, pp)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 

@@ -209,6 +209,17 @@ pkv_status pkv_decode_step(const pkv_pool *pool, const void *q, const int32_t *b
  */
 int32_t pkv_plan_partition_pages(int32_t batch, int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t num_cus);
 
+/*
+ * The same plan for a batch whose longest context (tokens attended, the new one included) is
+ * max_context_len, a bound the caller's scheduler knows on the host: when every sequence fits in
+ * one partition of the planned size, no split is planned (min(max_blocks_per_seq, 256) is
+ * returned), so no merge kernel runs.  max_context_len < 0 means unknown (the plain plan); -1 on
+ * bad arguments.  Only the launch shape depends on it: a context longer than the bound is still
+ * attended correctly, through partitions of the returned size.
+ */
+int32_t pkv_plan_partition_pages_for_context(int32_t batch, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                                             int32_t max_context_len, int32_t num_cus);
+
 /* Workspace bytes needed for the given positive partition size (after the same 256-page cap
  * the attention call applies); 0 without a split.  Returns 0 on bad arguments. */
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_blocks_per_seq,

@@ -73,6 +73,7 @@ SIGNATURES = {
          ctypes.c_float, _c_int32, _vp, _c_size, _vp],
     ),
     "pkv_plan_partition_pages": (_c_int32, [_c_int32, _c_int32, _c_int32, _c_int32]),
+    "pkv_plan_partition_pages_for_context": (_c_int32, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32]),
     "pkv_decode_workspace_bytes": (_c_size, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "pkv_device_cu_count": (_c_int32, []),
     "pkv_validate_append_host": (ctypes.c_int, [_vp, _c_int32, _vp, _c_int32, _c_int32, _vp]),
@@ -191,12 +192,16 @@ def cu_count(device=None) -> int:
     return n
 
 
-def plan_partition_pages(batch: int, num_kv_heads: int, max_blocks_per_seq: int, num_cus: int | None = None) -> int:
-    key = (batch, num_kv_heads, max_blocks_per_seq, num_cus)
+def plan_partition_pages(batch: int, num_kv_heads: int, max_blocks_per_seq: int, num_cus: int | None = None,
+                         max_context: int | None = None) -> int:
+    """Pages per partition; ``max_context`` (the longest context of the batch, when the caller
+    knows it on the host) lets a batch whose sequences all fit one partition skip the split."""
+    mc = -1 if max_context is None else int(max_context)
+    key = (batch, num_kv_heads, max_blocks_per_seq, num_cus, mc)
     r = _plans.get(key)
     if r is None:
         cus = cu_count() if num_cus is None else int(num_cus)
-        r = int(library().pkv_plan_partition_pages(batch, num_kv_heads, max_blocks_per_seq, cus))
+        r = int(library().pkv_plan_partition_pages_for_context(batch, num_kv_heads, max_blocks_per_seq, mc, cus))
         if r <= 0:
             raise ValueError("invalid planning arguments")
         if num_cus is not None:
@@ -284,12 +289,13 @@ def rope_kv_append(k_pool, v_pool, block_tables, positions, q, k_new, v_new, cos
 
 
 def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=None, *, out_dtype=None, scale=None,
-                           partition_pages: int = 0, workspace=None, stream=None):
+                           partition_pages: int = 0, max_context: int | None = None, workspace=None, stream=None):
     """Decode attention of q [B][Hq][D] over each sequence's pages; returns out [B][Hq][D].
 
     ``out_dtype`` is torch.bfloat16 (default) or torch.float32; ``scale`` defaults to
-    1/sqrt(head_dim).  ``partition_pages`` <= 0 lets the library plan the context split; when no
-    workspace is passed, a torch buffer cached per (device, stream) is used.
+    1/sqrt(head_dim).  ``partition_pages`` <= 0 lets the library plan the context split (with
+    ``max_context``, the longest context if the caller knows it, a batch that fits one partition
+    is not split); when no workspace is passed, a torch buffer cached per (device, stream) is used.
     """
     torch = _torch()
     _dev_tensor("q", q, torch.bfloat16, 3)
@@ -315,7 +321,7 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=No
         scale = 1.0 / float(dim) ** 0.5
     pp = int(partition_pages)
     if pp <= 0:
-        pp = plan_partition_pages(batch, hkv, max_blocks, cu_count(q.device))
+        pp = plan_partition_pages(batch, hkv, max_blocks, cu_count(q.device), max_context)
     need = decode_workspace_bytes(batch, hq, max_blocks, pp)
     sh = _stream_handle(stream, q.device)
     ws_ptr, ws_bytes = None, 0
@@ -334,7 +340,7 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=No
 
 
 def decode_step(q, k_pool, v_pool, block_tables, positions, k_new, v_new, out=None, *, out_dtype=None, scale=None,
-                partition_pages: int = 0, workspace=None, stream=None):
+                partition_pages: int = 0, max_context: int | None = None, workspace=None, stream=None):
     """kv_append then decode attention over positions + 1 tokens, in one launch; returns out."""
     torch = _torch()
     _dev_tensor("q", q, torch.bfloat16, 3)
@@ -364,7 +370,7 @@ def decode_step(q, k_pool, v_pool, block_tables, positions, k_new, v_new, out=No
         scale = 1.0 / float(dim) ** 0.5
     pp = int(partition_pages)
     if pp <= 0:
-        pp = plan_partition_pages(batch, hkv, max_blocks, cu_count(q.device))
+        pp = plan_partition_pages(batch, hkv, max_blocks, cu_count(q.device), max_context)
     need = decode_workspace_bytes(batch, hq, max_blocks, pp)
     sh = _stream_handle(stream, q.device)
     ws_ptr, ws_bytes = None, 0

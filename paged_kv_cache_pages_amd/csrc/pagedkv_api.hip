@@ -85,6 +85,17 @@ extern "C" int32_t pkv_plan_partition_pages(int32_t batch, int32_t num_kv_heads,
   return pages >= cap ? cap : (int32_t)pages;
 }
 
+extern "C" int32_t pkv_plan_partition_pages_for_context(int32_t batch, int32_t num_kv_heads,
+                                                        int32_t max_blocks_per_seq, int32_t max_context_len,
+                                                        int32_t num_cus) {
+  const int32_t pages = pkv_plan_partition_pages(batch, num_kv_heads, max_blocks_per_seq, num_cus);
+  if (pages <= 0 || max_context_len < 0) return pages;
+  const int64_t longest = ((int64_t)max_context_len + pkv::kBlock - 1) / pkv::kBlock;
+  const int32_t cap = max_blocks_per_seq < pkv::kMaxPartitionPages ? max_blocks_per_seq : pkv::kMaxPartitionPages;
+  // Every sequence in one partition: a split would only add the merge launch.
+  return longest <= pages ? cap : pages;
+}
+
 namespace {
 // Pages per partition actually used for a requested (positive) size.
 int32_t resolved_partition_pages(int32_t requested, int32_t max_blocks_per_seq) {

@@ -58,6 +58,23 @@ def test_partition_planning():
     assert pkv.library().pkv_plan_partition_pages(-1, 8, 128, 256) == -1
 
 
+def test_partition_planning_with_a_known_longest_context():
+    plan = lambda b, t, mc: pkv.plan_partition_pages(b, 8, t, num_cus=256, max_context=mc)
+    assert plan(1, 128, 37) == 128  # 3 pages fit one 8-page partition: no split, no merge
+    assert plan(1, 128, 128) == 128  # 8 pages: still one partition
+    assert plan(1, 128, 129) == 8  # 9 pages: the plain plan
+    assert plan(1, 128, 2048) == 8
+    assert plan(17, 128, 320) == 128 and plan(17, 128, 321) == 20
+    assert plan(1, 300, 37) == 256  # the 256-page cap
+    assert plan(256, 128, 2048) == 128
+    for b in (1, 5, 16, 17, 40):
+        assert plan(b, 128, None) == pkv.plan_partition_pages(b, 8, 128, num_cus=256)
+    lib = pkv.library()
+    assert lib.pkv_plan_partition_pages_for_context(1, 8, 128, -1, 256) == 8
+    assert lib.pkv_plan_partition_pages_for_context(1, 8, 128, 0, 256) == 128
+    assert lib.pkv_plan_partition_pages_for_context(1, 0, 128, 37, 256) == -1
+
+
 def test_workspace_bytes():
     assert pkv.decode_workspace_bytes(4, 32, 128, 128) == 0
     assert pkv.decode_workspace_bytes(4, 32, 128, 200) == 0

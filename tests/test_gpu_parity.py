@@ -105,6 +105,23 @@ def test_ragged_lengths_and_splits(gpu, partition_pages):
     assert_close(out.cpu().numpy(), ref, f"ragged pp={partition_pages}")
 
 
+def test_known_longest_context_plans_no_split(gpu):
+    """With the longest context known on the host, a batch that fits one partition runs unsplit:
+    the result is the unsplit kernel's bit for bit, and a context longer than the bound is still
+    attended correctly through partitions."""
+    w = make_custom(seed=23, lengths=[37, 5, 100, 128])
+    d = upload(w)
+    args = (gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"])
+    assert gpu.plan_partition_pages(w.batch, 8, w.max_blocks, max_context=128) == w.max_blocks
+    planned = attend(*args, max_context=128)
+    unsplit = attend(*args, partition_pages=w.max_blocks)
+    assert np.array_equal(planned.cpu().numpy(), unsplit.cpu().numpy())
+    ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens)
+    assert_close(planned.cpu().numpy(), ref, "planned with max_context")
+    low = attend(*args, max_context=1)  # a wrong (too small) bound changes only the launch shape
+    assert_close(low.cpu().numpy(), ref, "bound below the real context")
+
+
 def test_split_matches_unsplit(gpu):
     w = make_custom(seed=22, lengths=[3, 100, 700, 2048, 1500, 64])
     d = upload(w)
