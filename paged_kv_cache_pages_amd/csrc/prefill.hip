@@ -17,7 +17,8 @@
 // 16 A-operand rows of key tile t mapped to keys 8 (r / 4) + 4 t + r % 4 of a 32-key half step.
 // Then lane l holds, for query l % 16, exactly keys 8 (l / 16) .. 8 (l / 16) + 7 of the half in
 // its two C tiles, which is the B-operand layout of P^T in O^T = V^T P^T: the probabilities
-// never leave their registers.  V is staged transposed in LDS so that V^T rows are contiguous.
+// never leave their registers.  V is staged row-major like K; the A operand of V^T comes from the
+// transposing LDS read (ds_read_b64_tr_b16), so no transpose happens at staging.
 // The probabilities enter the second product as two BF16 terms (hi + lo), so the weights keep
 // about 16 significant bits; Q, K and V are BF16 inputs and are exact in the products.
 #include <type_traits>
@@ -32,12 +33,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 64;                 // keys per step (four pages), two 32-key halves
 constexpr int kVecPerRow = kHeadDim * 2 / 16;  // 16-byte vectors per 64-wide BF16 row
-constexpr int kKStride = kHeadDim + 8;     // BF16 elements per staged K row (144 bytes)
-constexpr int kVStride = kChunk + 8;       // BF16 elements per staged V^T row (144 bytes)
+constexpr int kKStride = kHeadDim + 8;     // BF16 elements per staged K or V row (144 bytes)
 
 // Packed rows of sequence b, or false when they fall outside [0, num_tokens) or exceed the
 // prompt-length bound the grid was sized for (such a sequence is left untouched).
@@ -104,7 +106,7 @@ constexpr int kLdsPages = 256;  // block-table entries kept in LDS (4096 tokens)
 template <int kSub, bool kOutBf16>
 __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillParams p, int32_t tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kChunk * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kHeadDim * kVStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kChunk * kKStride];
   __shared__ int32_t s_pages[kLdsPages];
   constexpr int kRows = 16 * kSub;  // query rows per workgroup
 
@@ -197,12 +199,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       *reinterpret_cast<u32x4 *>(&s_k[buf][st_key * kKStride + st_dim + 32 * e]) = x.k[e];
-      uint16_t *vt = &s_vt[buf][(st_dim + 32 * e) * kVStride + st_key];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        vt[(2 * w) * kVStride] = (uint16_t)(x.v[e][w] & 0xFFFFu);
-        vt[(2 * w + 1) * kVStride] = (uint16_t)(x.v[e][w] >> 16);
-      }
+      *reinterpret_cast<u32x4 *>(&s_v[buf][st_key * kKStride + st_dim + 32 * e]) = x.v[e];
     }
   };
 
@@ -322,10 +319,21 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
 
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs) {
+      // V^T fragments straight from the row-major V rows with the transposing LDS read: within
+      // each 16-lane group, lane L of the read receives element L % 4 of the 4-element rows read
+      // by lanes L / 4 + 4 i, i = 0..3.  So lane M reads row key0 + M / 4 at dims 4 (M % 4) ..
+      // + 3 of the tile, and lane (j, r) ends up with keys key0 .. key0 + 3 of dim r; two reads
+      // (key0 = 32 hs + 8 j and + 4) give the 8 keys of the A operand.
       u32x4 vf[4];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        vf[dt] = *reinterpret_cast<const u32x4 *>(&s_vt[buf][(16 * dt + r) * kVStride + 32 * hs + 8 * j]);
+      for (int dt = 0; dt < 4; ++dt) {
+        const uint16_t *vrow = &s_v[buf][(32 * hs + 8 * j + (r >> 2)) * kKStride + 16 * dt + 4 * (r & 3)];
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)vrow);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16 *)(vrow + 4 * kKStride));
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), c = __builtin_bit_cast(u32x2, hi);
+        vf[dt] = u32x4{a[0], a[1], c[0], c[1]};
+      }
 #pragma unroll
       for (int sub = 0; sub < kSub; ++sub) {
         // Each weight is carried as a sum of two BF16 values (hi + lo, ~16 significant bits):
