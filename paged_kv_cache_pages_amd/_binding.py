@@ -213,14 +213,18 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, max_blocks_per_seq: int
     return int(library().pkv_decode_workspace_bytes(batch, num_q_heads, max_blocks_per_seq, partition_pages))
 
 
-def _cached_workspace(nbytes: int, device, stream_handle):
+def _cached_workspace(nbytes: int, device, stream):
     """A workspace tensor kept per (device, stream) and grown on demand.  Calls on one stream are
-    ordered, so reusing its workspace is safe; other streams get their own."""
+    ordered, so reusing its workspace is safe; other streams get their own.  The tensor is
+    allocated on the stream that uses it, so when a larger one replaces it, torch's allocator
+    hands the old memory out again only to later work on that same stream."""
     torch = _torch()
-    key = (device.index, stream_handle)
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (device.index, s.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -327,7 +331,7 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=No
     ws_ptr, ws_bytes = None, 0
     if need > 0:
         if workspace is None:
-            workspace = _cached_workspace(need, q.device, sh)
+            workspace = _cached_workspace(need, q.device, stream)
         _dev_tensor("workspace", workspace, workspace.dtype)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = library().pkv_paged_decode_attention(
@@ -376,7 +380,7 @@ def decode_step(q, k_pool, v_pool, block_tables, positions, k_new, v_new, out=No
     ws_ptr, ws_bytes = None, 0
     if need > 0:
         if workspace is None:
-            workspace = _cached_workspace(need, q.device, sh)
+            workspace = _cached_workspace(need, q.device, stream)
         _dev_tensor("workspace", workspace, workspace.dtype)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     pool = Pool(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, hkv, dim, block)
