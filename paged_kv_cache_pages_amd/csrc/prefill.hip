@@ -284,18 +284,23 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
         for (int e = 0; e < 8; ++e)
           pe[sub][hs][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][hs][e >> 2][e & 3], c_log2, -m[sub]));
     };
+    // On a tile's first step the anchor is still -inf, so the exact maximum is taken at once
+    // instead of computing the weights twice.
+    const bool first = c == 0;
     bool over = false;
+    if (!first) {
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub) {
-      weights(sub);
-      float pm = 0.0f;
+      for (int sub = 0; sub < kSub; ++sub) {
+        weights(sub);
+        float pm = 0.0f;
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
+        for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) pm = __builtin_fmaxf(pm, __builtin_fmaxf(pe[sub][hs][e], pe[sub][hs][e + 1]));
-      over |= !(pm <= kHeadroomScale);  // NaN only while m = -inf
+          for (int e = 0; e < 8; e += 2) pm = __builtin_fmaxf(pm, __builtin_fmaxf(pe[sub][hs][e], pe[sub][hs][e + 1]));
+        over |= !(pm <= kHeadroomScale);
+      }
     }
-    if (__builtin_amdgcn_ballot_w64(over)) {  // wave-uniform
+    if (first || __builtin_amdgcn_ballot_w64(over)) {  // wave-uniform
 #pragma unroll
       for (int sub = 0; sub < kSub; ++sub) {
         float mx = -INFINITY;
