@@ -201,20 +201,21 @@ pkv_status pkv_decode_step(const pkv_pool *pool, const void *q, const int32_t *b
                            int32_t partition_pages, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Pages per partition chosen when partition_pages <= 0.  Pure function (no GPU needed):
- * no split when batch * num_kv_heads workgroups already cover the device, otherwise the
- * smallest multiple of 4 pages (at least 8) that yields about 4 workgroups per compute unit;
- * never more than 256.  Returns min(max_blocks_per_seq, 256) when no split is needed; -1 on bad
- * arguments.
+ * Pages per partition chosen when partition_pages <= 0.  Pure function (no GPU needed).  With L
+ * the pages of the longest context (here the table width): no split when L <= 48 (the merge
+ * launch would cost more than the split saves) or when the batch * num_kv_heads workgroups number
+ * between 3/4 of num_cus and num_cus; otherwise the smallest multiple of 4 pages (at least 8) that
+ * gives about 2 workgroups per compute unit over L, and no split if that is >= L; never more than
+ * 256.  Returns min(max_blocks_per_seq, 256) when no split is planned; -1 on bad arguments.
  */
 int32_t pkv_plan_partition_pages(int32_t batch, int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t num_cus);
 
 /*
  * The same plan for a batch whose longest context (tokens attended, the new one included) is
- * max_context_len, a bound the caller's scheduler knows on the host: when every sequence fits in
- * one partition of the planned size, no split is planned (min(max_blocks_per_seq, 256) is
- * returned), so no merge kernel runs.  max_context_len < 0 means unknown (the plain plan); -1 on
- * bad arguments.  Only the launch shape depends on it: a context longer than the bound is still
+ * max_context_len, a bound the caller's scheduler knows on the host: L is then that context's
+ * pages instead of the table width, so short batches run unsplit (no merge kernel) and long ones
+ * split by their real length.  max_context_len < 0 means unknown (the plain plan); -1 on bad
+ * arguments.  Only the launch shape depends on it: a context longer than the bound is still
  * attended correctly, through partitions of the returned size.
  */
 int32_t pkv_plan_partition_pages_for_context(int32_t batch, int32_t num_kv_heads, int32_t max_blocks_per_seq,

@@ -49,9 +49,13 @@ def test_partition_planning():
     plan = lambda b, h, t, c: pkv.plan_partition_pages(b, h, t, num_cus=c)
     assert plan(256, 8, 128, 256) == 128  # 2048 (sequence, head) workgroups: no split
     assert plan(1, 8, 128, 256) == 8  # one long sequence: 16 partitions of 8 pages (the minimum)
-    assert plan(16, 8, 128, 256) == 16
-    assert plan(17, 8, 128, 256) == 20
+    assert plan(8, 8, 128, 256) == 16  # about 2 workgroups per compute unit
+    assert plan(16, 8, 128, 256) == 32
+    assert plan(17, 8, 128, 256) == 32
+    assert plan(24, 8, 128, 256) == 128 and plan(32, 8, 128, 256) == 128  # 3/4 to 1 workgroup per CU
+    assert plan(40, 8, 128, 256) == 64  # 320 workgroups: two partitions even out the CUs
     assert plan(64, 8, 128, 256) == 128
+    assert plan(4, 8, 48, 256) == 48 and plan(4, 8, 49, 256) == 8  # tables of at most 48 pages never split
     for b in range(0, 300, 7):
         p = plan(b, 8, 128, 256)
         assert 8 <= p <= 128 and (p == 128 or p % 4 == 0)
@@ -60,11 +64,13 @@ def test_partition_planning():
 
 def test_partition_planning_with_a_known_longest_context():
     plan = lambda b, t, mc: pkv.plan_partition_pages(b, 8, t, num_cus=256, max_context=mc)
-    assert plan(1, 128, 37) == 128  # 3 pages fit one 8-page partition: no split, no merge
-    assert plan(1, 128, 128) == 128  # 8 pages: still one partition
-    assert plan(1, 128, 129) == 8  # 9 pages: the plain plan
+    assert plan(1, 128, 37) == 128  # 3 pages: no split, no merge
+    assert plan(1, 128, 768) == 128  # 48 pages: still unsplit
+    assert plan(1, 128, 769) == 8  # 49 pages: split
     assert plan(1, 128, 2048) == 8
-    assert plan(17, 128, 320) == 128 and plan(17, 128, 321) == 20
+    assert plan(17, 128, 856) == 16  # 54 pages over 4 partitions
+    assert plan(17, 128, 2048) == 32
+    assert plan(40, 128, 1024) == 32 and plan(40, 128, 2048) == 64
     assert plan(1, 300, 37) == 256  # the 256-page cap
     assert plan(256, 128, 2048) == 128
     for b in (1, 5, 16, 17, 40):
