@@ -53,12 +53,16 @@ def test_continuous_batching_loop(gpu, static):
             assert st == 0, (st, bad)
             positions = np.array([pos[r] for r in rows], dtype=np.int32)
             print(f"[loop static={static}] step {steps} batch {len(rows)} max_pos {positions.max()}", flush=True)
-            pp = 4 if steps % 2 else 0  # alternate a forced 4-page split with the planned one
+            # rotate: the plan from the longest context (which the loop knows), a forced 4-page
+            # split, and the plan from the table width alone
+            pp = (0, 4, 0)[steps % 3]
+            longest = int(positions.max()) + 1 if steps % 3 == 0 else None
             for layer in range(layers):
                 q = normal_bf16(rng, (len(rows), HQ, D))
                 kn, vn = normal_bf16(rng, (len(rows), HKV, D)), normal_bf16(rng, (len(rows), HKV, D))
                 out = gpu.decode_step(to_gpu_bf16(q), kp, vp, to_gpu_i32(tables[layer]), to_gpu_i32(positions),
-                                      to_gpu_bf16(kn), to_gpu_bf16(vn), out_dtype=torch.float32, partition_pages=pp)
+                                      to_gpu_bf16(kn), to_gpu_bf16(vn), out_dtype=torch.float32, partition_pages=pp,
+                                      max_context=longest)
                 k_ref, v_ref = oracle.kv_append(k_ref, v_ref, tables[layer], positions, kn, vn)
                 ref = oracle.paged_decode_attention(q, k_ref, v_ref, tables[layer], positions + 1)
                 torch.cuda.synchronize()
