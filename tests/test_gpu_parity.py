@@ -367,6 +367,35 @@ def test_runs_on_the_callers_stream(gpu):
     assert torch.equal(out, ref)
 
 
+def test_concurrent_streams_do_not_interfere(gpu):
+    """The library keeps no per-call state: two streams running split decode steps on different
+    data at the same time, each with its own workspace, give what each gives alone."""
+    import torch
+
+    wa, wb = make_custom(seed=41, lengths=[2048, 900, 33]), make_custom(seed=42, lengths=[1500, 1, 700, 2048, 64])
+    da, db = upload(wa), upload(wb)
+    alone = [attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"], partition_pages=8)
+             for d in (da, db)]
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = {0: [], 1: []}
+    for s in (sa, sb):
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(10):
+        for i, (s, d, w) in enumerate(((sa, da, wa), (sb, db, wb))):
+            with torch.cuda.stream(s):
+                ws = torch.zeros(gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, 8), dtype=torch.uint8,
+                                 device="cuda") if rep == 0 else None
+                if rep == 0:
+                    outs[i].append(ws)
+                outs[i].append(attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                                      partition_pages=8, workspace=outs[i][0]))
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        for out in outs[i][1:]:
+            assert torch.equal(out, alone[i])
+
+
 def test_batch_zero_is_a_no_op(gpu):
     import torch
 
