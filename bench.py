@@ -288,22 +288,27 @@ def run(args):
     samples = []
 
     def timed(phases):
-        """Run K steps made of ``phases`` (callables, run in order); HIP events on the launch stream
-        bracket every phase.  Returns (wall seconds for K steps, per-phase mean ms)."""
+        """Run K steps made of ``phases`` (callables, run in order) by wall clock with nothing else
+        in the timed region, then K more with HIP events on the launch stream around every phase.
+        Returns (wall seconds for the first K steps, per-phase mean ms from the second K)."""
         for _ in range(args.warmup):
             for f in phases:
                 f()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            for f in phases:
+                f()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(K)]
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for i in range(K):
             for j, f in enumerate(phases):
                 ev[i][j].record()
                 f()
             ev[i][len(phases)].record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         per = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(len(phases))]
         samples.append(per)
         return wall, [float(np.mean(x)) for x in per]
