@@ -286,6 +286,7 @@ def run(args):
 
     K = args.steps
     samples = []
+    regions = []
 
     def timed(phases):
         """Run K steps made of ``phases`` (callables, run in order) by wall clock with nothing else
@@ -295,12 +296,16 @@ def run(args):
             for f in phases:
                 f()
         torch.cuda.synchronize()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        r0.record()
         for _ in range(K):
             for f in phases:
                 f()
+        r1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        regions.append(r0.elapsed_time(r1) / K)  # GPU ms per step over the timed region
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(K)]
         torch.cuda.synchronize()
         for i in range(K):
@@ -410,7 +415,9 @@ def run(args):
     # One "launch" = one layer.  Dominant kernel: the fused decode kernel (attention + append
     # bytes) or, for the two-call step, the attention kernel (attention bytes).
     if fused_mode:
-        launch_ms = fused_ms / w.layers
+        # the fused step is one launch per layer: the events bracketing the timed region give the
+        # launches' average duration with nothing else between them
+        launch_ms = regions[1] / w.layers
         launch_bytes = step_bytes // w.layers
         kernel = "paged_decode_kernel (fused append)"
     else:
@@ -435,9 +442,10 @@ def run(args):
         del graph
         return e0.elapsed_time(e1) / reps
 
-    # The roofline uses the mean of the per-launch events.  Back-to-back launches replayed from one
-    # graph are reported beside it: they remove host launch gaps (which matter for short kernels)
-    # but add the graph's node-to-node gap (bw256: 171.7 vs 168.4 us, rocprof 166.2 us).
+    # The roofline uses the events bracketing the timed region (fused step) or the per-launch
+    # events (attention of the two-call step).  Back-to-back launches replayed from one graph are
+    # reported beside it: they remove host launch gaps (which matter for short kernels) but add
+    # the graph's node-to-node gap.
     reps = max(10, min(K, 100))
     launch_ms_graph = graph_launch_ms(fused_all if fused_mode else attend_all, reps) / w.layers
     achieved = gbps(launch_bytes, launch_ms)
@@ -500,7 +508,9 @@ def run(args):
             "kernel": kernel,
             "algorithmic_bytes_per_launch": launch_bytes,
             "us_per_launch": round(launch_ms * 1e3, 3),
-            "timing": "mean of HIP events around each launch, on the launch stream",
+            "timing": ("HIP events bracketing the K timed steps on the launch stream, per layer launch"
+                       if fused_mode else "mean of HIP events around each launch, on the launch stream"),
+            "us_per_launch_events": round((fused_ms if fused_mode else attn_ms) / w.layers * 1e3, 3),
             "us_per_launch_graph": round(launch_ms_graph * 1e3, 3),
         },
         "note": "The reference pages report no throughput or hardware numbers for this kernel; "
