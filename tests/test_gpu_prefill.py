@@ -116,6 +116,24 @@ def test_prefill_rows_equal_decode_kernel(gpu):
     assert np.all(np.abs(a - b) <= 4e-3 + 2e-2 * np.abs(b))
 
 
+def test_prefill_behind_prefixes_longer_than_the_staged_table(gpu):
+    """The kernel keeps the first 256 table entries (4096 tokens) in LDS and reads the rest from
+    HBM: prompt chunks behind cached prefixes of 4050 to 4200 tokens in a 300-page table read
+    both, and match the oracle."""
+    import torch
+
+    lens, starts = [48, 30, 5], [4200, 4050, 4090]
+    w = make_prefill(27, lens, starts, max_blocks=300)
+    print(f"[prefill] long prefixes lens={lens} starts={starts}", flush=True)
+    d = upload(w)
+    out = run(gpu, d, torch.float32)
+    torch.cuda.synchronize()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, w.v_new)
+    assert np.array_equal(bf16_to_bits(d["k_pool"]), rk) and np.array_equal(bf16_to_bits(d["v_pool"]), rv)
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos)
+    assert_close(out.cpu().numpy(), ref, "long prefixes")
+
+
 def test_prefill_ignores_stale_slots_and_unused_pages(gpu):
     import torch
 

@@ -83,3 +83,73 @@ def test_continuous_batching_loop(gpu, static):
     assert s["largest_batch"] >= 2 and steps > 20
     if not static:
         assert s["admission_waits"] > 0  # the pool is small enough that requests queue
+
+
+def test_prefill_then_decode_loop(gpu):
+    """Admitted prompts are written and attended by the paged prefill kernels in one batched call
+    per layer (each prompt's causal attention checked against the prefill oracle), then decode
+    steps continue from the pages prefill wrote, checked against the decode oracle."""
+    import torch
+
+    rng = np.random.default_rng(21)
+    layers, max_blocks, num_pages = 2, 24, 2 * 48
+    alloc = gpu.PageAllocator(num_pages, layers, max_blocks, free_order=rng.permutation(num_pages))
+    k_ref = normal_bf16(rng, (num_pages, HKV, 16, D))
+    v_ref = normal_bf16(rng, (num_pages, HKV, 16, D))
+    kp, vp = to_gpu_bf16(k_ref), to_gpu_bf16(v_ref)
+    reqs = {rid: (int(rng.integers(1, 200)), int(rng.integers(1, 30))) for rid in range(10)}
+    for rid, (p, n) in reqs.items():
+        assert alloc.submit(rid, p, n) == 0
+    pos, left, done, steps, prefills = {}, {}, 0, 0, 0
+    while done < len(reqs):
+        admitted = alloc.admit()
+        if admitted:
+            lens = [reqs[r][0] for r in admitted]
+            for rid, p in zip(admitted, lens):
+                for t in range(0, p, 16):
+                    assert alloc.ensure(rid, t) == 0
+            cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            start = np.zeros(len(lens), dtype=np.int32)
+            print(f"[prefill loop] prefill of {len(lens)} prompts, {int(cu[-1])} rows", flush=True)
+            for layer in range(layers):
+                bt = np.stack([alloc.table(r)[layer] for r in admitted]).astype(np.int32)
+                q = normal_bf16(rng, (int(cu[-1]), HQ, D))
+                kn, vn = normal_bf16(rng, (int(cu[-1]), HKV, D)), normal_bf16(rng, (int(cu[-1]), HKV, D))
+                d_bt, d_cu, d_st = to_gpu_i32(bt), to_gpu_i32(cu), to_gpu_i32(start)
+                gpu.prefill_kv_append(kp, vp, d_bt, d_cu, d_st, to_gpu_bf16(kn), to_gpu_bf16(vn))
+                out = gpu.paged_prefill_attention(to_gpu_bf16(q), kp, vp, d_bt, d_cu, d_st, out_dtype=torch.float32)
+                k_ref, v_ref = oracle.prefill_kv_append(k_ref, v_ref, bt, cu, start, kn, vn)
+                ref = oracle.paged_prefill_attention(q, k_ref, v_ref, bt, cu, start)
+                torch.cuda.synchronize()
+                assert_close(out.cpu().numpy(), ref, f"prefill {prefills} layer {layer}")
+            prefills += 1
+            for rid, p in zip(admitted, lens):
+                pos[rid], left[rid] = p, min(reqs[rid][1], max_blocks * 16 - p) - 1
+        rows = sorted(r for r in pos if left[r] > 0)
+        if rows:
+            st, bad, tables = alloc.prepare_step(rows, [pos[r] for r in rows])
+            assert st == 0, (st, bad)
+            positions = np.array([pos[r] for r in rows], dtype=np.int32)
+            for layer in range(layers):
+                q = normal_bf16(rng, (len(rows), HQ, D))
+                kn, vn = normal_bf16(rng, (len(rows), HKV, D)), normal_bf16(rng, (len(rows), HKV, D))
+                out = gpu.decode_step(to_gpu_bf16(q), kp, vp, to_gpu_i32(tables[layer]), to_gpu_i32(positions),
+                                      to_gpu_bf16(kn), to_gpu_bf16(vn), out_dtype=torch.float32,
+                                      partition_pages=4 if steps % 2 else 0)
+                k_ref, v_ref = oracle.kv_append(k_ref, v_ref, tables[layer], positions, kn, vn)
+                ref = oracle.paged_decode_attention(q, k_ref, v_ref, tables[layer], positions + 1)
+                torch.cuda.synchronize()
+                assert_close(out.cpu().numpy(), ref, f"step {steps} layer {layer}")
+            steps += 1
+        for r in list(pos):
+            if left[r] > 0:
+                pos[r] += 1
+                left[r] -= 1
+            if left[r] <= 0:
+                assert alloc.release(r) == 0
+                del pos[r], left[r]
+                done += 1
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_bits(kp), k_ref) and np.array_equal(bf16_to_bits(vp), v_ref)
+    assert prefills >= 2 and steps > 10
+    assert alloc.stats()["free_pages"] == num_pages
