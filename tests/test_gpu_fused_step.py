@@ -36,15 +36,17 @@ def test_fused_step_equals_two_calls(gpu, name):
     import torch
 
     w = make_config(name)
-    print(f"[fused] config={name} B={w.batch} layers={w.layers}", flush=True)
+    # the launch configuration bench.py times: the plan from the longest context
+    pp = gpu.plan_partition_pages(w.batch, 8, w.max_blocks, max_context=int(w.context_lens.max()))
+    print(f"[fused] config={name} B={w.batch} layers={w.layers} partition_pages={pp}", flush=True)
     kp1, vp1 = to_gpu_bf16(w.k_pool), to_gpu_bf16(w.v_pool)
     kp2, vp2 = kp1.clone(), vp1.clone()
     pos, lens = to_gpu_i32(w.positions), to_gpu_i32(w.context_lens)
     ref_k, ref_v = w.k_pool, w.v_pool
     for layer in range(w.layers):
         t = layer_tensors(w, layer)
-        a = two_calls(gpu, t["q"], kp1, vp1, t["block_tables"], pos, lens, t["k_new"], t["v_new"], 0)
-        b = fused(gpu, t["q"], kp2, vp2, t["block_tables"], pos, t["k_new"], t["v_new"], 0)
+        a = two_calls(gpu, t["q"], kp1, vp1, t["block_tables"], pos, lens, t["k_new"], t["v_new"], pp)
+        b = fused(gpu, t["q"], kp2, vp2, t["block_tables"], pos, t["k_new"], t["v_new"], pp)
         torch.cuda.synchronize()
         assert torch.equal(a, b), f"layer {layer}"
         if layer == 0 or layer == w.layers - 1:

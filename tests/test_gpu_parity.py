@@ -80,6 +80,8 @@ def test_attention_parity(gpu, name):
         gpu.kv_append(kp, vp, t["block_tables"], pos, t["k_new"], t["v_new"])
         out32 = attend(gpu, t["q"], kp, vp, t["block_tables"], lens)
         out16 = attend(gpu, t["q"], kp, vp, t["block_tables"], lens, out_dtype=torch.bfloat16)
+        # the plan bench.py times: from the longest context, which the host knows
+        out_bench = attend(gpu, t["q"], kp, vp, t["block_tables"], lens, max_context=int(w.context_lens.max()))
         torch.cuda.synchronize()
         ref_k, ref_v = oracle.kv_append(ref_k, ref_v, w.block_tables[layer], w.positions, w.k_new[layer], w.v_new[layer])
         ref = oracle.paged_decode_attention(w.q[layer], ref_k, ref_v, w.block_tables[layer], w.context_lens, 0.125,
@@ -88,6 +90,7 @@ def test_attention_parity(gpu, name):
         sel = slice(None) if rows is None else rows
         abs_err, rel_err = assert_close(got[sel], ref[sel], f"{name} layer {layer}")
         print(f"  layer {layer}: max abs {abs_err:.3e}, max rel {rel_err:.3e}", flush=True)
+        assert_close(out_bench.cpu().numpy()[sel], ref[sel], f"{name} layer {layer}, bench plan")
         assert np.array_equal(bf16_to_bits(out16), oracle.bf16_round_nearest_even(got))
 
 
