@@ -15,8 +15,9 @@
 //     merged in LDS at the end with the pairwise (max, sum) rule.
 //   * One 16-token page of one KV head is a contiguous 2 KiB run.  A wavefront loads it with
 //     two 16-byte loads per lane (lane = 8 * token + chunk): lanes 0..63 cover bytes 0..1023
-//     (tokens 0..7), the second load bytes 1024..2047 (tokens 8..15).  The next page's K and V
-//     are in flight while the current page is computed.
+//     (tokens 0..7), the second load bytes 1024..2047 (tokens 8..15).  The next two pages' K and
+//     V are in flight while the current page is computed (a short chain issues all its loads
+//     at once).
 //   * QK: each lane forms 8-element partial dots with v_dot2_f32_bf16 (BF16 pairs, FP32
 //     accumulate) and the 8 lanes of a token are summed with three DPP adds.
 //   * Softmax in log2 units with a lazily moved anchor: scores are compared with the anchor
@@ -25,7 +26,8 @@
 //   * PV: each lane accumulates p * V for its 8 dims and 4 heads in 32 FP32 registers; the
 //     token lanes are summed once at the end.
 //   * Long contexts with few (sequence, KV head) pairs are cut into partitions; each writes its
-//     (max, sum, partial output) per query head and a merge kernel combines them.
+//     (max, sum, partial output) per query head and a merge kernel combines them.  Workgroup ids
+//     are partition-major, so every partition index is spread over all 8 XCDs.
 // Block-table entries are read straight into a VGPR (one entry per lane) and moved to scalar
 // registers with v_readlane; every entry is range-checked before a page is touched.
 #include <math.h>
