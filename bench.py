@@ -279,10 +279,14 @@ def run(args):
             pkv.paged_decode_attention(t["q"], kp, vp, t["bt"], lens, t["out"], partition_pages=pp,
                                        workspace=workspace)
 
+    # The fused step goes through PreparedDecodeStep: the same pkv_decode_step launch with its
+    # arguments checked once, so an eager loop is not bound by Python argument handling.
+    prepared = [pkv.PreparedDecodeStep(t["q"], kp, vp, t["bt"], pos, t["k_new"], t["v_new"], t["out"],
+                                       partition_pages=pp, workspace=workspace) for t in layers]
+
     def fused_all():
-        for t in layers:
-            pkv.decode_step(t["q"], kp, vp, t["bt"], pos, t["k_new"], t["v_new"], t["out"], partition_pages=pp,
-                            workspace=workspace)
+        for step in prepared:
+            step()
 
     K = args.steps
     samples = []
@@ -465,7 +469,7 @@ def run(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "compute": "bf16 inputs, f32 accumulate and softmax",
-        "step": "fused: pkv_decode_step, one launch per layer" if fused_mode
+        "step": "fused: pkv_decode_step (PreparedDecodeStep), one launch per layer" if fused_mode
                 else "two-call: pkv_kv_append + pkv_paged_decode_attention per layer",
         "launch": "hip graph replay of the whole step" if args.graph else "eager launches through the C ABI",
         "data": "synthetic (seeded N(0,1) BF16; no dataset)",

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     STATUS_NAMES,
     PagedKVError,
     Pool,
+    PreparedDecodeStep,
     cu_count,
     decode_step,
     decode_workspace_bytes,

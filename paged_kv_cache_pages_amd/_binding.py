@@ -393,6 +393,76 @@ def decode_step(q, k_pool, v_pool, block_tables, positions, k_new, v_new, out=No
     return out
 
 
+class PreparedDecodeStep:
+    """pkv_decode_step on fixed buffers, for loops that reuse the same tensors and update their
+    contents in place.  Shapes, dtypes, the partition plan, the workspace and the stream are
+    checked and chosen once (as decode_step does on every call); each call then passes the cached
+    arguments straight to the library, on ``stream`` if one was given, else on the stream current
+    at the call (so the step can be captured into a graph).  The tensors are kept alive by this
+    object; their contents (q, block_tables, positions, k_new, v_new, the pools) are read at
+    launch time."""
+
+    def __init__(self, q, k_pool, v_pool, block_tables, positions, k_new, v_new, out, *, scale=None,
+                 partition_pages: int = 0, max_context: int | None = None, workspace=None, stream=None):
+        torch = _torch()
+        _dev_tensor("q", q, torch.bfloat16, 3)
+        _dev_tensor("k_pool", k_pool, torch.bfloat16, 4)
+        _dev_tensor("v_pool", v_pool, torch.bfloat16, 4)
+        _dev_tensor("block_tables", block_tables, torch.int32, 2)
+        _dev_tensor("positions", positions, torch.int32, 1)
+        _dev_tensor("k_new", k_new, torch.bfloat16, 3)
+        _dev_tensor("v_new", v_new, torch.bfloat16, 3)
+        if not isinstance(out, torch.Tensor) or out.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("out must be a bfloat16 or float32 tensor")
+        _dev_tensor("out", out, out.dtype, 3)
+        batch, hq, dim = q.shape
+        num_pages, hkv, block, _ = k_pool.shape
+        if tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != (batch, hq, dim):
+            raise ValueError("inconsistent pool / out shapes")
+        if block_tables.shape[0] != batch or positions.shape[0] != batch:
+            raise ValueError("block_tables / positions batch differs from q")
+        if tuple(k_new.shape) != (batch, hkv, dim) or k_new.shape != v_new.shape:
+            raise ValueError("k_new / v_new must be [batch][kv_heads][head_dim]")
+        max_blocks = block_tables.shape[1]
+        scale = 1.0 / float(dim) ** 0.5 if scale is None else float(scale)
+        pp = int(partition_pages)
+        if pp <= 0:
+            pp = plan_partition_pages(batch, hkv, max_blocks, cu_count(q.device), max_context)
+        need = decode_workspace_bytes(batch, hq, max_blocks, pp)
+        ws_ptr, ws_bytes = None, 0
+        if need > 0:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            _dev_tensor("workspace", workspace, workspace.dtype)
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+            if ws_bytes < need:
+                raise ValueError(f"workspace holds {ws_bytes} bytes, {need} needed")
+        self.out = out
+        self.partition_pages = pp
+        self._keep = (q, k_pool, v_pool, block_tables, positions, k_new, v_new, out, workspace)
+        self._pool = Pool(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, hkv, dim, block)
+        self._fn = library().pkv_decode_step
+        self._args = (
+            ctypes.byref(self._pool), q.data_ptr(), block_tables.data_ptr(), max_blocks, positions.data_ptr(),
+            k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(),
+            PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32, batch, hq, scale, pp, ws_ptr, ws_bytes,
+        )
+        self._stream = None if stream is None else _stream_handle(stream, q.device)
+        self._device = q.device
+        # torch's raw current-stream query is ~10x cheaper per call than current_stream()
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        index = q.device.index
+        self._current = (lambda: raw(index)) if raw is not None else (
+            lambda: torch.cuda.current_stream(self._device).cuda_stream)
+
+    def __call__(self):
+        sh = self._stream if self._stream is not None else self._current()
+        st = self._fn(*self._args, sh)
+        if st != PKV_OK:
+            raise PagedKVError("pkv_decode_step", st)
+        return self.out
+
+
 def _prefill_args(k_pool, v_pool, block_tables, cu_seqlens, start_pos, max_prompt_len):
     torch = _torch()
     _dev_tensor("k_pool", k_pool, torch.bfloat16, 4)
