@@ -125,6 +125,27 @@ def test_known_longest_context_plans_no_split(gpu):
     assert_close(low.cpu().numpy(), ref, "bound below the real context")
 
 
+@pytest.mark.parametrize("partition_pages", [0, 2])
+def test_large_batch_of_short_contexts(gpu, partition_pages):
+    """4096 sequences of 1..64 tokens: a grid of 32768 (sequence, KV head) workgroups unsplit, or
+    twice that with 2-page partitions and the merge, against the oracle on every sequence."""
+    import torch
+
+    rng = np.random.default_rng(55)
+    lengths = rng.integers(1, 65, size=4096).tolist()
+    w = make_custom(seed=56, lengths=lengths, max_blocks=4)
+    print(f"[large batch] B={w.batch} pages={w.num_pages} partition_pages={partition_pages}", flush=True)
+    d = upload(w)
+    gpu.kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["positions"], d["k_new"], d["v_new"])
+    out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                 partition_pages=partition_pages)
+    torch.cuda.synchronize()
+    rk, rv = oracle.kv_append(w.k_pool, w.v_pool, w.block_tables[0], w.positions, w.k_new[0], w.v_new[0])
+    assert np.array_equal(bf16_to_bits(d["k_pool"]), rk) and np.array_equal(bf16_to_bits(d["v_pool"]), rv)
+    ref = oracle.paged_decode_attention(w.q[0], rk, rv, w.block_tables[0], w.context_lens)
+    assert_close(out.cpu().numpy(), ref, f"large batch pp={partition_pages}")
+
+
 def test_split_matches_unsplit(gpu):
     w = make_custom(seed=22, lengths=[3, 100, 700, 2048, 1500, 64])
     d = upload(w)
