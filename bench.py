@@ -599,7 +599,10 @@ def prefill_leg(args, torch, pkv):
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic("prefill_attention", PREFILL_TRAFFIC_PROFILE, PREFILL_SOURCE)
                      if args.prefill_config == "prefill16x512" else None,
-                     "kernel": "prefill_attention_kernel", "algorithmic_flops_per_launch": flops},
+                     # the launch picks 32-key steps (prefill_attention_kernel_k32) from four
+                     # workgroups per compute unit, as at 16 x 512, else prefill_attention_kernel
+                     "kernel": "prefill attention (prefill_attention_kernel[_k32])",
+                     "algorithmic_flops_per_launch": flops},
     }
 
 

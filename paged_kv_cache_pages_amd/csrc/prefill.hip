@@ -5,9 +5,10 @@
 //
 // The article materialises a [tokens][tokens] BF16 score matrix per head, masks it, runs a
 // softmax kernel over it and multiplies by V with library GEMMs.  Here no score matrix exists:
-// a workgroup owns 16 query rows of one sequence and the 4 query heads of one KV head (one head
-// per wavefront), streams the sequence's pages 64 keys at a time through LDS, and runs both
-// products on the matrix cores (v_mfma_f32_16x16x32_bf16) with an FP32 online softmax in between.
+// a workgroup owns 16 or 32 query rows of one sequence and the 4 query heads of one KV head (one
+// head per wavefront), streams the sequence's pages 64 (or 32) keys at a time through LDS, and
+// runs both products on the matrix cores (v_mfma_f32_16x16x32_bf16) with an FP32 online softmax
+// in between.
 //
 // Register layout of the 16x16x32 BF16 MFMA on gfx950 (lane l, element i):
 //   A operand: row l % 16, reduction index 8 (l / 16) + i
@@ -37,7 +38,6 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 64;                 // keys per step (four pages), two 32-key halves
 constexpr int kVecPerRow = kHeadDim * 2 / 16;  // 16-byte vectors per 64-wide BF16 row
 constexpr int kKStride = kHeadDim + 8;     // BF16 elements per staged K or V row (144 bytes)
 
@@ -103,8 +103,12 @@ __device__ __forceinline__ void store_row4(void *out, int64_t elem, f32x4 v) {
 // gives up that order and unbalances the XCDs when prompts differ in length.)
 constexpr int kLdsPages = 256;  // block-table entries kept in LDS (4096 tokens); the rest from HBM
 
-template <int kSub, bool kOutBf16>
-__global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillParams p, int32_t tiles) {
+// kChunk keys per step: 64 (two 32-key halves; 166 VGPRs with kSub = 2, 3 waves per SIMD) or 32
+// (one half; fits 128 VGPRs, so 4 waves per SIMD, at twice the steps and barriers per key).
+template <int kSub, int kChunk, bool kOutBf16>
+__device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, int32_t tiles) {
+  constexpr int kHalves = kChunk / 32;  // 32-key halves per step
+  constexpr int kVecs = kChunk / 32;    // 16-byte K (and V) vectors each thread stages per step
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kChunk * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kChunk * kKStride];
   __shared__ int32_t s_pages[kLdsPages];
@@ -167,10 +171,10 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
     }
   }
 
-  // Staging: thread -> key (tid % 64) of the step, dims d0 .. d0 + 7 and d0 + 32 .. d0 + 39 with
-  // d0 = 8 (tid / 64).
-  const int st_key = tid & 63;
-  const int st_dim = (tid >> 6) * 8;
+  // Staging: thread -> key (tid % kChunk) of the step and dims d0 .. d0 + 7 (and d0 + 32 .. d0 + 39
+  // for 64-key steps) with d0 = 8 (tid / kChunk).
+  const int st_key = tid & (kChunk - 1);
+  const int st_dim = (tid / kChunk) * 8;
   // Page ids run one step ahead of the data: the id of step c + 1 is in hand when that step's K/V
   // loads issue, so no load inside a step waits on another.  A key past the tile's last query
   // reads the sequence's first page instead (validated, so in bounds); its V row is zeroed when
@@ -181,23 +185,25 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
     return e < kLdsPages ? s_pages[e] : table[e];
   };
   struct Rows {
-    u32x4 k[2], v[2];
+    u32x4 k[kVecs], v[kVecs];
   };
   auto load_step = [&](int c, int32_t pg, Rows &x) {
     const int kp = c * kChunk + st_key;
     const int64_t off = (((int64_t)pg * p.num_kv_heads + g) * kBlock + kp % kBlock) * kHeadDim + st_dim;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < kVecs; ++e) {
       x.k[e] = *reinterpret_cast<const u32x4 *>(p.k_pool + off + 32 * e);
       x.v[e] = *reinterpret_cast<const u32x4 *>(p.v_pool + off + 32 * e);
     }
   };
   auto stage = [&](int c, int buf, Rows &x) {
     if (c * kChunk + kChunk > n_keys) {  // the last step only: no stale NaN reaches V
-      if (c * kChunk + st_key >= n_keys) x.v[0] = x.v[1] = u32x4{0, 0, 0, 0};
+      if (c * kChunk + st_key >= n_keys)
+#pragma unroll
+        for (int e = 0; e < kVecs; ++e) x.v[e] = u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < kVecs; ++e) {
       *reinterpret_cast<u32x4 *>(&s_k[buf][st_key * kKStride + st_dim + 32 * e]) = x.k[e];
       *reinterpret_cast<u32x4 *>(&s_v[buf][st_key * kKStride + st_dim + 32 * e]) = x.v[e];
     }
@@ -238,9 +244,9 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
     }
 
     // S^T for the four 16-key tiles of the step (half hs, tile t), every column block.
-    f32x4 s[kSub][2][2];
+    f32x4 s[kSub][kHalves][2];
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
+    for (int hs = 0; hs < kHalves; ++hs)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int key_row = 32 * hs + 8 * (r >> 2) + 4 * t + (r & 3);
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
         // this lane holds keys c * kChunk + 8 j + 32 hs + 4 t + i for query first_q + 16 sub + r
         const int room = first_q + 16 * sub + r - (c * kChunk + 8 * j);
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs)
+        for (int hs = 0; hs < kHalves; ++hs)
 #pragma unroll
           for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -276,10 +282,10 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
     // 2^8 (or is infinite: always so on the first step, where m = -inf); that test runs on the
     // exp2 results, which need no NaN canonicalisation before v_max3, and the exact row maximum
     // is taken only on the rare step that moves the anchor.
-    float pe[kSub][2][8];
+    float pe[kSub][kHalves][8];
     auto weights = [&](int sub) {
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
+      for (int hs = 0; hs < kHalves; ++hs)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           pe[sub][hs][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][hs][e >> 2][e & 3], c_log2, -m[sub]));
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
         weights(sub);
         float pm = 0.0f;
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs)
+        for (int hs = 0; hs < kHalves; ++hs)
 #pragma unroll
           for (int e = 0; e < 8; e += 2) pm = __builtin_fmaxf(pm, __builtin_fmaxf(pe[sub][hs][e], pe[sub][hs][e + 1]));
         over |= !(pm <= kHeadroomScale);
@@ -305,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
       for (int sub = 0; sub < kSub; ++sub) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs)
+        for (int hs = 0; hs < kHalves; ++hs)
 #pragma unroll
           for (int t = 0; t < 2; ++t)
             mx = fmaxf(mx, fmaxf(fmaxf(s[sub][hs][t][0], s[sub][hs][t][1]), fmaxf(s[sub][hs][t][2], s[sub][hs][t][3])));
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
     }
 
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
+    for (int hs = 0; hs < kHalves; ++hs) {
       // V^T fragments straight from the row-major V rows with the transposing LDS read: within
       // each 16-lane group, lane L of the read receives element L % 4 of the 4-element rows read
       // by lanes L / 4 + 4 i, i = 0..3.  So lane M reads row key0 + M / 4 at dims 4 (M % 4) ..
@@ -386,6 +392,18 @@ __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillPara
   }
 }
 
+
+template <int kSub, bool kOutBf16>
+__global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillParams p, int32_t tiles) {
+  prefill_attention_body<kSub, 64, kOutBf16>(p, tiles);
+}
+
+template <int kSub, bool kOutBf16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void prefill_attention_kernel_k32(
+    PrefillParams p, int32_t tiles) {
+  prefill_attention_body<kSub, 32, kOutBf16>(p, tiles);
+}
+
 }  // namespace
 
 hipError_t launch_prefill_append(const PrefillParams &p, hipStream_t stream) {
@@ -397,28 +415,36 @@ hipError_t launch_prefill_append(const PrefillParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int kSub>
+template <int kSub, bool kK32>
 hipError_t launch_attention(const PrefillParams &p, bool out_bf16, hipStream_t stream) {
   const int64_t tiles = ((int64_t)p.max_prompt_len + 16 * kSub - 1) / (16 * kSub);
   const int64_t blocks = tiles * p.batch * p.num_kv_heads;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (out_bf16)
-    hipLaunchKernelGGL((prefill_attention_kernel<kSub, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p,
-                       (int32_t)tiles);
-  else
-    hipLaunchKernelGGL((prefill_attention_kernel<kSub, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p,
-                       (int32_t)tiles);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if constexpr (kK32) {
+    if (out_bf16) hipLaunchKernelGGL((prefill_attention_kernel_k32<kSub, true>), grid, block, 0, stream, p, (int32_t)tiles);
+    else hipLaunchKernelGGL((prefill_attention_kernel_k32<kSub, false>), grid, block, 0, stream, p, (int32_t)tiles);
+  } else {
+    if (out_bf16) hipLaunchKernelGGL((prefill_attention_kernel<kSub, true>), grid, block, 0, stream, p, (int32_t)tiles);
+    else hipLaunchKernelGGL((prefill_attention_kernel<kSub, false>), grid, block, 0, stream, p, (int32_t)tiles);
+  }
   return hipGetLastError();
 }
 
 // Two 16-query blocks per wavefront halve the LDS traffic, staging and barriers per score (16
 // prompts x 512: 55.6 vs 64.1 us) but halve the workgroup count; below two workgroups per compute
 // unit (one 512-token prompt: 128 workgroups) one block per wavefront is faster (11.8 vs 15.5 us).
+// From four workgroups per compute unit the grid keeps every SIMD busy and 32-key steps at 4
+// waves per SIMD hide more latency than 64-key steps at 3 (16 x 512: 46.6-48.4 vs 51.1-51.7 us);
+// with fewer workgroups the longer chain of steps costs more (six chunked prompts, 3 per CU:
+// 39.2 vs 37.1 us; one 512-token prompt 12.5 vs 10.7 us).
 hipError_t launch_prefill_attention(const PrefillParams &p, bool out_bf16, int32_t num_cus, hipStream_t stream) {
   const int64_t tiles2 = ((int64_t)p.max_prompt_len + 31) / 32;
-  if (tiles2 * p.batch * p.num_kv_heads >= 2 * (int64_t)num_cus) return launch_attention<2>(p, out_bf16, stream);
-  return launch_attention<1>(p, out_bf16, stream);
+  const int64_t groups2 = tiles2 * p.batch * p.num_kv_heads;
+  if (groups2 >= 4 * (int64_t)num_cus) return launch_attention<2, true>(p, out_bf16, stream);
+  if (groups2 >= 2 * (int64_t)num_cus) return launch_attention<2, false>(p, out_bf16, stream);
+  return launch_attention<1, false>(p, out_bf16, stream);
 }
 
 }  // namespace pkv
