@@ -7,10 +7,11 @@ resident in HBM before timing starts.  The default workload is 256 sequences at 
 (32768 pages, 1 GiB of BF16 K+V).
 
 Prints ONE JSON line.  ``value`` is algorithmic GB/s of the whole step (bytes / wall time per
-step); ``roofline`` reports the attention kernel against the 8 TB/s HBM peak using HIP events
-recorded around each launch on the stream the kernel runs on; ``cpu_baseline`` times the FP64 CPU
-oracle on the host cores.  The pages report no throughput or hardware numbers for this kernel,
-so ``vs_baseline`` is null.
+step, with nothing but the step's launches in the timed region); ``roofline`` reports the fused
+decode kernel against the 8 TB/s HBM peak using the HIP events that bracket the timed steps on
+the stream the kernel runs on (one launch per layer); ``prefill`` adds the paged prefill
+kernels on a second workload; ``cpu_baseline`` times the FP64 CPU oracle on the host cores.  The
+pages report no throughput or hardware numbers for this kernel, so ``vs_baseline`` is null.
 """
 
 from __future__ import annotations
