@@ -112,6 +112,7 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kChunk * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kChunk * kKStride];
   __shared__ int32_t s_pages[kLdsPages];
+  __shared__ int32_t s_bad[kThreads / 64];
   constexpr int kRows = 16 * kSub;  // query rows per workgroup
 
   const uint32_t pairs = gridDim.x / (uint32_t)tiles;  // batch * num_kv_heads
@@ -125,39 +126,22 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   const int r = lane & 15;                 // this lane's query column within each block of 16
   const int j = lane >> 4;                 // this lane's group of 8 keys / 8 dims
 
+  // The prologue is a chain of dependent reads; each one is issued as soon as its address is
+  // known: start_pos with cu_seqlens (b < batch by construction of the grid; the empty asm
+  // consumes it before the early return, so the compiler cannot sink the load below it), the
+  // tile's Q rows (inside the checked prompt) before the table pass.
+  const int32_t start = p.start_pos[b];
   int32_t row0, n;
-  if (!sequence_rows(p, b, row0, n)) return;
+  const bool rows_ok = sequence_rows(p, b, row0, n);
+  asm volatile("" ::"s"(start));
+  if (!rows_ok) return;
   const int q_lo = tile * kRows;
   if (q_lo >= n) return;
   const int q_rows = min(kRows, n - q_lo);
-  const int32_t start = p.start_pos[b];
   const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks;
-
-  // The whole sequence must be addressable: every page up to its last prompt position.
-  int bad = !(start >= 0 && (int64_t)start + n <= (int64_t)p.max_blocks * kBlock);
-  if (!bad) {
-    const int need = (start + n + kBlock - 1) / kBlock;
-    for (int e = tid; e < need; e += kThreads) {
-      const int32_t pg = table[e];
-      bad |= pg < 0 || pg >= p.num_pages;
-      if (e < kLdsPages) s_pages[e] = pg;
-    }
-  }
-  bad = __syncthreads_or(bad);  // also publishes s_pages
   auto out_elem = [&](int sub) -> int64_t {  // first of this lane's outputs of block `sub`
     return (((int64_t)row0 + q_lo + 16 * sub + r) * p.num_q_heads + h) * kHeadDim + 4 * j;
   };
-  if (bad) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int sub = 0; sub < kSub; ++sub)
-      if (16 * sub + r < q_rows)
-        for (int dt = 0; dt < 4; ++dt) store_row4<kOutBf16>(p.out, out_elem(sub) + 16 * dt, zero);
-    return;
-  }
-
-  const int n_keys = start + q_lo + q_rows;  // keys 0 .. last query position of the tile
-  const int n_chunks = (n_keys + kChunk - 1) / kChunk;
 
   // Q^T as the B operand of S^T = K Q^T: query column r of block sub, dims 32 half + 8 j .. + 7.
   u32x4 qf[kSub][2];
@@ -170,6 +154,37 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
       qf[sub][1] = src[4 + j];
     }
   }
+
+  // The whole sequence must be addressable: every page up to its last prompt position.
+  int bad = !(start >= 0 && (int64_t)start + n <= (int64_t)p.max_blocks * kBlock);
+  if (!bad) {
+    const int need = (start + n + kBlock - 1) / kBlock;
+    for (int e = tid; e < need; e += kThreads) {
+      const int32_t pg = table[e];
+      bad |= pg < 0 || pg >= p.num_pages;
+      if (e < kLdsPages) s_pages[e] = pg;
+    }
+  }
+  // Workgroup OR of `bad`: one flag per wavefront in LDS and one barrier, which also publishes
+  // s_pages.  (__syncthreads_or would read the workgroup size from the dispatch arguments with
+  // two dependent global loads and take three barriers.)
+  const bool wave_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+  if (lane == 0) s_bad[tid >> 6] = wave_bad;
+  __syncthreads();
+  bad = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) bad |= s_bad[w];
+  if (bad) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub)
+      if (16 * sub + r < q_rows)
+        for (int dt = 0; dt < 4; ++dt) store_row4<kOutBf16>(p.out, out_elem(sub) + 16 * dt, zero);
+    return;
+  }
+
+  const int n_keys = start + q_lo + q_rows;  // keys 0 .. last query position of the tile
+  const int n_chunks = (n_keys + kChunk - 1) / kChunk;
 
   // Staging: thread -> key (tid % kChunk) of the step and dims d0 .. d0 + 7 (and d0 + 32 .. d0 + 39
   // for 64-key steps) with d0 = 8 (tid / kChunk).
