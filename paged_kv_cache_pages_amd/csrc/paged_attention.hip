@@ -231,11 +231,42 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   const int b = pair / p.num_kv_heads;
   const int qh0 = g * kGroup;  // first query head of the group
 
+  const int p0 = part * p.part_pages;
+  const int tok = lane >> 3;    // token within each half page
+  const int chunk = lane & 7;   // 16-byte chunk of the row: dims 8*chunk .. 8*chunk+7
+
+  // Reads whose addresses do not depend on the context length go out before it is known, so the
+  // prologue is one round trip: this wavefront's table entries (lane k: logical page
+  // p0 + wave + kWaves * k, read while it lies inside the sequence's table row), q, and in the
+  // fused step the new token's K/V row.
+  const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
+  const int e_lane = p0 + wave + kWaves * lane;
+  const int ids_row = e_lane < p.max_blocks ? bt[e_lane] : 0;
+  uint32_t qv[kGroup][4];
+  {
+    const uint16_t *qb = p.q + ((int64_t)b * p.num_q_heads + qh0) * kHeadDim + chunk * 8;
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      const uint4 t = load16(qb + h * kHeadDim);
+      qv[h][0] = t.x; qv[h][1] = t.y; qv[h][2] = t.z; qv[h][3] = t.w;
+    }
+  }
+  uint4 knew = make_uint4(0u, 0u, 0u, 0u), vnew = knew;
+  if (kFused) {
+    const int64_t row = ((int64_t)b * p.num_kv_heads + g) * kHeadDim + chunk * 8;
+    knew = load16(p.k_new + row);
+    vnew = load16(p.v_new + row);
+  }
   const int L = context_length<kFused>(p, b);
   const bool len_ok = L >= 0 && L <= p.max_blocks * kBlock;
   const int n_pages = len_ok ? (L + kBlock - 1) / kBlock : 0;
-  const int p0 = part * p.part_pages;
   const int p1 = min(p0 + p.part_pages, n_pages);
+  // Keep those reads above the branch below (the compiler would otherwise sink them past it,
+  // behind the length read).
+  asm volatile("" ::"v"(ids_row));
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h) asm volatile("" ::"v"(qv[h][0]), "v"(qv[h][1]), "v"(qv[h][2]), "v"(qv[h][3]));
+  if (kFused) asm volatile("" ::"v"(knew.x), "v"(knew.y), "v"(knew.z), "v"(knew.w), "v"(vnew.x), "v"(vnew.y), "v"(vnew.z), "v"(vnew.w));
 
   if (p0 >= p1) {
     if (kSplit) return;  // empty partition (or empty/invalid sequence): the merge handles it
@@ -246,26 +277,14 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
     return;
   }
 
-  const int tok = lane >> 3;    // token within each half page
-  const int chunk = lane & 7;   // 16-byte chunk of the row: dims 8*chunk .. 8*chunk+7
   const float c_log2 = p.score_log2;
 
   // Pages of this wavefront: local index k -> logical page p0 + wave + kWaves * k, k < n_w <= 64
   // (a partition holds at most kMaxPartitionPages pages).
   int n_w = (p1 - p0 - wave + kWaves - 1) / kWaves;
   if (n_w < 0) n_w = 0;
-  uint32_t qv[kGroup][4];
-  {
-    const uint16_t *qb = p.q + ((int64_t)b * p.num_q_heads + qh0) * kHeadDim + chunk * 8;
-#pragma unroll
-    for (int h = 0; h < kGroup; ++h) {
-      const uint4 t = load16(qb + h * kHeadDim);
-      qv[h][0] = t.x; qv[h][1] = t.y; qv[h][2] = t.z; qv[h][3] = t.w;
-    }
-  }
-  const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks + p0 + wave;
   // One table entry per lane, range-checked before any page is touched.
-  const int ids = lane < n_w ? bt[(int64_t)kWaves * lane] : 0;
+  const int ids = lane < n_w ? ids_row : 0;
   const bool bad = __builtin_amdgcn_ballot_w64(ids < 0 || ids >= p.num_pages) != 0;
   // The wavefront holding the sequence's last page (it always holds the new token).
   const bool holds_last = n_w > 0 && p1 == n_pages && p0 + wave + kWaves * (n_w - 1) == n_pages - 1;
@@ -275,12 +294,6 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   const bool do_append = kFused && last_id >= 0 && last_id < p.num_pages;
   if (bad) n_w = 0;
   const bool owns_last = n_w > 0 && holds_last;
-  uint4 knew = make_uint4(0u, 0u, 0u, 0u), vnew = knew;
-  if (do_append) {
-    const int64_t row = ((int64_t)b * p.num_kv_heads + g) * kHeadDim + chunk * 8;
-    knew = load16(p.k_new + row);
-    vnew = load16(p.v_new + row);
-  }
   // q and the table entries must have landed before the first page load is issued (the page
   // addresses need the entries anyway).  Waiting here explicitly also tells the compiler that q
   // is resident inside the page loop, so the loop's waits only count the page loads in flight.
