@@ -266,6 +266,43 @@ def test_invalid_page_id_zeroes_only_that_sequence(gpu, partition_pages, bad_ent
     assert np.array_equal(out[0], good[0]) and np.array_equal(out[2], good[2])
 
 
+@pytest.mark.parametrize("partition_pages", [0, 4, 128])
+def test_table_entries_past_the_context_are_ignored(gpu, partition_pages):
+    """The kernel reads each wavefront's table entries before it knows the context length (every
+    read stays inside the row of max_blocks entries); entries past a sequence's own pages must
+    change nothing, whatever they hold: out-of-range values give bit-identical outputs and pools,
+    for the attention call and for the fused step."""
+    import torch
+
+    w = make_custom(seed=37, lengths=[1, 16, 17, 300, 2047, 0])
+    junk = np.array([-1, w.num_pages, 1 << 30, -(1 << 31), (1 << 31) - 1], dtype=np.int64)
+    bt = w.block_tables[0].astype(np.int64)
+    dirty_bt = bt.copy()
+    for b, n in enumerate(w.context_lens):
+        used = (int(n) + 15) // 16
+        tail = dirty_bt[b, used:]
+        tail[:] = junk[np.arange(tail.size) % junk.size]
+    print(f"[parity] junk past the context, partition_pages={partition_pages}", flush=True)
+    d = upload(w)
+    clean = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                   partition_pages=partition_pages)
+    dirty = attend(gpu, d["q"], d["k_pool"], d["v_pool"], to_gpu_i32(dirty_bt), d["context_lens"],
+                   partition_pages=partition_pages)
+    torch.cuda.synchronize()
+    assert torch.equal(clean, dirty)
+    # fused step: its context is positions + 1 = context_lens (the workloads' convention), so the
+    # same entries lie past it
+    assert np.array_equal(w.positions + 1, w.context_lens)
+    d1, d2 = upload(w), upload(w)
+    a = gpu.decode_step(d1["q"], d1["k_pool"], d1["v_pool"], d1["block_tables"], d1["positions"], d1["k_new"],
+                        d1["v_new"], out_dtype=torch.float32, partition_pages=partition_pages)
+    b = gpu.decode_step(d2["q"], d2["k_pool"], d2["v_pool"], to_gpu_i32(dirty_bt), d2["positions"], d2["k_new"],
+                        d2["v_new"], out_dtype=torch.float32, partition_pages=partition_pages)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(d1["k_pool"], d2["k_pool"]) and torch.equal(d1["v_pool"], d2["v_pool"])
+
+
 def test_invalid_context_length_zeroes_sequence(gpu):
     w = make_custom(seed=30, lengths=[20, 50])
     d = upload(w)
