@@ -154,7 +154,9 @@ pkv_status pkv_rope_kv_append(const pkv_pool *pool, const int32_t *block_tables,
  *
  *   q                 device bf16[batch][num_q_heads][head_dim]
  *   k_pool, v_pool    device bf16[num_pages][num_kv_heads][block_size][head_dim]
- *   block_tables      device int32[batch][max_blocks_per_seq]
+ *   block_tables      device int32[batch][max_blocks_per_seq]; the whole buffer must be
+ *                     readable (a workgroup may read entries past its sequence's context
+ *                     before it knows the length); entries past the context are ignored
  *   context_lens      device int32[batch]; tokens attended, including the one just appended;
  *                     0 gives an all-zero output row
  *   out               device, bf16 or f32 [batch][num_q_heads][head_dim] per out_dtype
