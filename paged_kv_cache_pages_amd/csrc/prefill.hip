@@ -7,8 +7,8 @@
 // softmax kernel over it and multiplies by V with library GEMMs.  Here no score matrix exists:
 // a workgroup owns 16 or 32 query rows of one sequence and the 4 query heads of one KV head (one
 // head per wavefront), streams the sequence's pages 64 (or 32) keys at a time through LDS, and
-// runs both products on the matrix cores (v_mfma_f32_16x16x32_bf16) with an FP32 online softmax
-// in between.
+// runs both products on the matrix cores (v_mfma_f32_16x16x32_bf16 and _f16) with an FP32 online
+// softmax in between.
 //
 // Register layout of the 16x16x32 BF16 MFMA on gfx950 (lane l, element i):
 //   A operand: row l % 16, reduction index 8 (l / 16) + i
@@ -20,8 +20,12 @@
 // its two C tiles, which is the B-operand layout of P^T in O^T = V^T P^T: the probabilities
 // never leave their registers.  V is staged row-major like K; the A operand of V^T comes from the
 // transposing LDS read (ds_read_b64_tr_b16), so no transpose happens at staging.
-// The probabilities enter the second product as two BF16 terms (hi + lo), so the weights keep
-// about 16 significant bits; Q, K and V are BF16 inputs and are exact in the products.
+// Q and K enter the first product as the BF16 inputs they are (exact).  For the second product V
+// is staged as FP16, which holds every BF16 value up to 65280 exactly (smaller than 2^-14 in
+// magnitude only to within 2^-25), and the probabilities enter as FP16 (11 significant bits,
+// round to nearest even), so the second product needs one FP16 MFMA per tile.  A tile whose V
+// holds a larger magnitude (or an infinity) is computed again in a second pass with BF16 V and
+// each probability carried as two BF16 terms (hi + lo, about 16 significant bits).
 #include <type_traits>
 
 #include "pkv_internal.h"
@@ -36,6 +40,8 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kVecPerRow = kHeadDim * 2 / 16;  // 16-byte vectors per 64-wide BF16 row
@@ -79,6 +85,25 @@ __global__ __launch_bounds__(kThreads) void prefill_append_kernel(PrefillParams 
 __device__ __forceinline__ float wave_xor_max(float x, int mask) { return fmaxf(x, __shfl_xor(x, mask, 64)); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// Eight BF16 values to FP16 (exact for every finite BF16 value up to 65280; the next one, 65536,
+// becomes infinity), and the largest magnitude seen so far, so the caller can tell whether all
+// of them fit.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, float &amax) {
+  u32x4 y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_bit_cast(float, x[i] << 16);
+    const float hi = __builtin_bit_cast(float, x[i] & 0xFFFF0000u);
+    amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(lo), __builtin_fabsf(hi)));
+    f2 v;
+    v[0] = lo;
+    v[1] = hi;
+    y[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+  }
+  return y;
+}
 
 template <bool kOutBf16>
 __device__ __forceinline__ void store_row4(void *out, int64_t elem, f32x4 v) {
@@ -102,6 +127,7 @@ __device__ __forceinline__ void store_row4(void *out, int64_t elem, f32x4 v) {
 // light ones fill the tail.  (Grouping a sequence's tiles on one XCD for L2 reuse was slower: it
 // gives up that order and unbalances the XCDs when prompts differ in length.)
 constexpr int kLdsPages = 256;  // block-table entries kept in LDS (4096 tokens); the rest from HBM
+constexpr float kF16Max = 65504.0f;  // largest finite FP16 value
 
 // kChunk keys per step: 64 (two 32-key halves; 166 VGPRs with kSub = 2, 3 waves per SIMD) or 32
 // (one half; fits 128 VGPRs, so 4 waves per SIMD, at twice the steps and barriers per key).
@@ -110,9 +136,10 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   constexpr int kHalves = kChunk / 32;  // 32-key halves per step
   constexpr int kVecs = kChunk / 32;    // 16-byte K (and V) vectors each thread stages per step
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kChunk * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kChunk * kKStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kChunk * kKStride];  // FP16
   __shared__ int32_t s_pages[kLdsPages];
   __shared__ int32_t s_bad[kThreads / 64];
+  __shared__ int32_t s_wide[2];  // step index whose staged V holds a value past FP16's range
   constexpr int kRows = 16 * kSub;  // query rows per workgroup
 
   const uint32_t pairs = gridDim.x / (uint32_t)tiles;  // batch * num_kv_heads
@@ -170,6 +197,7 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   // two dependent global loads and take three barriers.)
   const bool wave_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
   if (lane == 0) s_bad[tid >> 6] = wave_bad;
+  if (tid < 2) s_wide[tid] = -1;
   __syncthreads();
   bad = 0;
 #pragma unroll
@@ -211,24 +239,25 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
       x.v[e] = *reinterpret_cast<const u32x4 *>(p.v_pool + off + 32 * e);
     }
   };
-  auto stage = [&](int c, int buf, Rows &x) {
+  // kWide = false: V is staged as FP16, and a step whose V holds a magnitude past FP16's largest
+  // finite value (or an infinity) marks itself in s_wide (the flag holds the step index, so flags
+  // of earlier steps never need clearing).  kWide = true: V is staged as BF16.
+  auto stage = [&](int c, int buf, Rows &x, auto wide_tag) {
+    constexpr bool kWide = decltype(wide_tag)::value;
     if (c * kChunk + kChunk > n_keys) {  // the last step only: no stale NaN reaches V
       if (c * kChunk + st_key >= n_keys)
 #pragma unroll
         for (int e = 0; e < kVecs; ++e) x.v[e] = u32x4{0, 0, 0, 0};
     }
+    float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < kVecs; ++e) {
       *reinterpret_cast<u32x4 *>(&s_k[buf][st_key * kKStride + st_dim + 32 * e]) = x.k[e];
-      *reinterpret_cast<u32x4 *>(&s_v[buf][st_key * kKStride + st_dim + 32 * e]) = x.v[e];
+      *reinterpret_cast<u32x4 *>(&s_v[buf][st_key * kKStride + st_dim + 32 * e]) =
+          kWide ? x.v[e] : bf16x8_to_f16x8(x.v[e], amax);
     }
+    if (!kWide && amax > kF16Max) s_wide[buf] = c;
   };
-
-  Rows rows;
-  load_step(0, page_of(0), rows);
-  int32_t pg_next = page_of(1);
-  stage(0, 0, rows);
-  __syncthreads();
 
   // Per column block: output tile, softmax anchor (log2 units, shared by the 4 lanes of a query;
   // it moves only when a weight exceeds 2^8, so most steps leave the accumulators alone) and the
@@ -236,167 +265,211 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   f32x4 o[kSub][4];
   f32x4 lsum[kSub];
   float m[kSub];
-#pragma unroll
-  for (int sub = 0; sub < kSub; ++sub) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[sub][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    lsum[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[sub] = -INFINITY;
-  }
   constexpr float kHeadroomScale = 256.0f;  // 2^8
-  const u32x4 kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // BF16 1.0 x 8
+  const u32x4 kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};     // BF16 1.0 x 8
+  const u32x4 kOnesF16 = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // FP16 1.0 x 8
   const float c_log2 = p.score_log2;
   const int first_q = start + q_lo;  // smallest query position of the tile
 
-  // One step; `buf` is a compile-time constant at both call sites (the loop is unrolled by two),
-  // so every LDS address of the step is a register base plus an immediate offset.
-  auto step = [&](int c, auto buf_tag) {
-    constexpr int buf = decltype(buf_tag)::value;
-    const bool more = c + 1 < n_chunks;
-    if (more) {  // in flight while this step computes
-      load_step(c + 1, pg_next, rows);
-      pg_next = page_of(c + 2);
+  // One pass over the tile's keys.  kWide = false: FP16 V and weights; returns whether a step met
+  // a V value past FP16's range (workgroup-uniform), in which case the caller runs the tile again
+  // with kWide = true: BF16 V and weights carried as hi + lo BF16 pairs.  (Two passes one after
+  // the other rather than a branch per step: with both product flavours inside the loop body the
+  // kernel no longer fits its registers.)
+  auto run = [&](auto wide_tag) -> bool {
+    constexpr bool kWide = decltype(wide_tag)::value;
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[sub][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      lsum[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m[sub] = -INFINITY;
     }
+    Rows rows;
+    load_step(0, page_of(0), rows);
+    int32_t pg_next = page_of(1);
+    stage(0, 0, rows, wide_tag);
+    __syncthreads();
+    bool any_wide = false;
 
-    // S^T for the four 16-key tiles of the step (half hs, tile t), every column block.
-    f32x4 s[kSub][kHalves][2];
-#pragma unroll
-    for (int hs = 0; hs < kHalves; ++hs)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int key_row = 32 * hs + 8 * (r >> 2) + 4 * t + (r & 3);
-        const uint16_t *krow = &s_k[buf][key_row * kKStride + 8 * j];
-        const u32x4 k0 = *reinterpret_cast<const u32x4 *>(krow);
-        const u32x4 k1 = *reinterpret_cast<const u32x4 *>(krow + 32);
-#pragma unroll
-        for (int sub = 0; sub < kSub; ++sub) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), as_bf16x8(qf[sub][0]), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), as_bf16x8(qf[sub][1]), acc, 0, 0, 0);
-          s[sub][hs][t] = acc;
-        }
+    // One step; `buf` is a compile-time constant at both call sites (the loop is unrolled by two),
+    // so every LDS address of the step is a register base plus an immediate offset.
+    auto step = [&](int c, auto buf_tag) {
+      constexpr int buf = decltype(buf_tag)::value;
+      const bool more = c + 1 < n_chunks;
+      if (more) {  // in flight while this step computes
+        load_step(c + 1, pg_next, rows);
+        pg_next = page_of(c + 2);
       }
 
-    // Causal mask, only on steps that reach past the tile's first query.
-    if (c * kChunk + kChunk - 1 > first_q) {
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
-        // this lane holds keys c * kChunk + 8 j + 32 hs + 4 t + i for query first_q + 16 sub + r
-        const int room = first_q + 16 * sub + r - (c * kChunk + 8 * j);
-#pragma unroll
-        for (int hs = 0; hs < kHalves; ++hs)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (32 * hs + 4 * t + i > room) s[sub][hs][t][i] = -INFINITY;
-      }
-    }
-
-    // Weights with the current anchor.  The anchor moves only when a weight of the step exceeds
-    // 2^8 (or is infinite: always so on the first step, where m = -inf); that test runs on the
-    // exp2 results, which need no NaN canonicalisation before v_max3, and the exact row maximum
-    // is taken only on the rare step that moves the anchor.
-    float pe[kSub][kHalves][8];
-    auto weights = [&](int sub) {
+      // S^T for the four 16-key tiles of the step (half hs, tile t), every column block.
+      f32x4 s[kSub][kHalves][2];
 #pragma unroll
       for (int hs = 0; hs < kHalves; ++hs)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pe[sub][hs][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][hs][e >> 2][e & 3], c_log2, -m[sub]));
+        for (int t = 0; t < 2; ++t) {
+          const int key_row = 32 * hs + 8 * (r >> 2) + 4 * t + (r & 3);
+          const uint16_t *krow = &s_k[buf][key_row * kKStride + 8 * j];
+          const u32x4 k0 = *reinterpret_cast<const u32x4 *>(krow);
+          const u32x4 k1 = *reinterpret_cast<const u32x4 *>(krow + 32);
+#pragma unroll
+          for (int sub = 0; sub < kSub; ++sub) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), as_bf16x8(qf[sub][0]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), as_bf16x8(qf[sub][1]), acc, 0, 0, 0);
+            s[sub][hs][t] = acc;
+          }
+        }
+
+      // Causal mask, only on steps that reach past the tile's first query.
+      if (c * kChunk + kChunk - 1 > first_q) {
+#pragma unroll
+        for (int sub = 0; sub < kSub; ++sub) {
+          // this lane holds keys c * kChunk + 8 j + 32 hs + 4 t + i for query first_q + 16 sub + r
+          const int room = first_q + 16 * sub + r - (c * kChunk + 8 * j);
+#pragma unroll
+          for (int hs = 0; hs < kHalves; ++hs)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (32 * hs + 4 * t + i > room) s[sub][hs][t][i] = -INFINITY;
+        }
+      }
+
+      // Weights with the current anchor.  The anchor moves only when a weight of the step exceeds
+      // 2^8 (or is infinite: always so on the first step, where m = -inf); that test runs on the
+      // exp2 results, which need no NaN canonicalisation before v_max3, and the exact row maximum
+      // is taken only on the rare step that moves the anchor.
+      float pe[kSub][kHalves][8];
+      auto weights = [&](int sub) {
+#pragma unroll
+        for (int hs = 0; hs < kHalves; ++hs)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pe[sub][hs][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][hs][e >> 2][e & 3], c_log2, -m[sub]));
+      };
+      // On a tile's first step the anchor is still -inf, so the exact maximum is taken at once
+      // instead of computing the weights twice.
+      const bool first = c == 0;
+      bool over = false;
+      if (!first) {
+#pragma unroll
+        for (int sub = 0; sub < kSub; ++sub) {
+          weights(sub);
+          float pm = 0.0f;
+#pragma unroll
+          for (int hs = 0; hs < kHalves; ++hs)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2)
+              pm = __builtin_fmaxf(pm, __builtin_fmaxf(pe[sub][hs][e], pe[sub][hs][e + 1]));
+          over |= !(pm <= kHeadroomScale);
+        }
+      }
+      if (first || __builtin_amdgcn_ballot_w64(over)) {  // wave-uniform
+#pragma unroll
+        for (int sub = 0; sub < kSub; ++sub) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int hs = 0; hs < kHalves; ++hs)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              mx = fmaxf(mx, fmaxf(fmaxf(s[sub][hs][t][0], s[sub][hs][t][1]),
+                                   fmaxf(s[sub][hs][t][2], s[sub][hs][t][3])));
+          mx = wave_xor_max(mx, 16);
+          mx = wave_xor_max(mx, 32);
+          mx *= c_log2;  // scale > 0; finite: key 0 is visible to every query in step 0
+          const float m_new = fmaxf(m[sub], mx);
+          const float alpha = __builtin_amdgcn_exp2f(m[sub] - m_new);
+          m[sub] = m_new;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) o[sub][dt] *= alpha;
+          lsum[sub] *= alpha;
+          weights(sub);
+        }
+      }
+
+      // O^T += V^T P^T for the step.  kWide: the weights as hi + lo BF16 pairs against BF16 V;
+      // otherwise as FP16 against the FP16 staged V.
+      auto pv = [&](auto wide_tag) {
+        constexpr bool kWide = decltype(wide_tag)::value;
+#pragma unroll
+        for (int hs = 0; hs < kHalves; ++hs) {
+          // V^T fragments straight from the row-major staged rows with the transposing LDS read:
+          // within each 16-lane group, lane L of the read receives element L % 4 of the 4-element
+          // rows read by lanes L / 4 + 4 i, i = 0..3.  So lane M reads row key0 + M / 4 at dims
+          // 4 (M % 4) .. + 3 of the tile, and lane (j, r) ends up with keys key0 .. key0 + 3 of
+          // dim r; two reads (key0 = 32 hs + 8 j and + 4) give the 8 keys of the A operand.
+          u32x4 vf[4];
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const uint16_t *vrow = &s_v[buf][(32 * hs + 8 * j + (r >> 2)) * kKStride + 16 * dt + 4 * (r & 3)];
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)vrow);
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16 *)(vrow + 4 * kKStride));
+            const u32x2 a = __builtin_bit_cast(u32x2, lo), b2v = __builtin_bit_cast(u32x2, hi);
+            vf[dt] = u32x4{a[0], a[1], b2v[0], b2v[1]};
+          }
+#pragma unroll
+          for (int sub = 0; sub < kSub; ++sub) {
+            if constexpr (!kWide) {
+              // The weights enter the product as FP16 (11 significant bits, round to nearest even).
+              u32x4 ph;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                f2 w2;
+                w2[0] = pe[sub][hs][2 * e];
+                w2[1] = pe[sub][hs][2 * e + 1];
+                ph[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, h2));
+              }
+              // One 16-dim tile at a time; the denominator rides along as an all-ones tile (every
+              // row of it is the query's sum of the same FP16 weights).
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt)
+                o[sub][dt] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(vf[dt]), as_f16x8(ph), o[sub][dt], 0, 0, 0);
+              lsum[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(kOnesF16), as_f16x8(ph), lsum[sub], 0, 0, 0);
+            } else {
+              // Each weight as a sum of two BF16 values (hi + lo, ~16 significant bits).
+              u32x4 ph, pl;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                f2 w2;
+                w2[0] = pe[sub][hs][2 * e];
+                w2[1] = pe[sub][hs][2 * e + 1];
+                const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, b2));
+                ph[e] = hi;
+                f2 rest;  // exact in FP32: each value minus its own BF16 rounding
+                rest[0] = w2[0] - __builtin_bit_cast(float, hi << 16);
+                rest[1] = w2[1] - __builtin_bit_cast(float, hi & 0xFFFF0000u);
+                pl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, b2));
+              }
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt) {
+                o[sub][dt] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[dt]), as_bf16x8(ph), o[sub][dt], 0, 0, 0);
+                o[sub][dt] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[dt]), as_bf16x8(pl), o[sub][dt], 0, 0, 0);
+              }
+              lsum[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kOnes), as_bf16x8(ph), lsum[sub], 0, 0, 0);
+              lsum[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kOnes), as_bf16x8(pl), lsum[sub], 0, 0, 0);
+            }
+          }
+        }
+      };
+      if constexpr (!kWide) any_wide |= s_wide[buf] == c;  // workgroup-uniform
+      pv(wide_tag);
+
+      if (more) stage(c + 1, buf ^ 1, rows, wide_tag);
+      __syncthreads();
     };
-    // On a tile's first step the anchor is still -inf, so the exact maximum is taken at once
-    // instead of computing the weights twice.
-    const bool first = c == 0;
-    bool over = false;
-    if (!first) {
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
-        weights(sub);
-        float pm = 0.0f;
-#pragma unroll
-        for (int hs = 0; hs < kHalves; ++hs)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) pm = __builtin_fmaxf(pm, __builtin_fmaxf(pe[sub][hs][e], pe[sub][hs][e + 1]));
-        over |= !(pm <= kHeadroomScale);
-      }
+    for (int c = 0; c < n_chunks; c += 2) {
+      step(c, std::integral_constant<int, 0>{});
+      if (c + 1 < n_chunks) step(c + 1, std::integral_constant<int, 1>{});
     }
-    if (first || __builtin_amdgcn_ballot_w64(over)) {  // wave-uniform
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int hs = 0; hs < kHalves; ++hs)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            mx = fmaxf(mx, fmaxf(fmaxf(s[sub][hs][t][0], s[sub][hs][t][1]), fmaxf(s[sub][hs][t][2], s[sub][hs][t][3])));
-        mx = wave_xor_max(mx, 16);
-        mx = wave_xor_max(mx, 32);
-        mx *= c_log2;  // scale > 0; finite: key 0 is visible to every query in step 0
-        const float m_new = fmaxf(m[sub], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[sub] - m_new);
-        m[sub] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[sub][dt] *= alpha;
-        lsum[sub] *= alpha;
-        weights(sub);
-      }
-    }
-
-#pragma unroll
-    for (int hs = 0; hs < kHalves; ++hs) {
-      // V^T fragments straight from the row-major V rows with the transposing LDS read: within
-      // each 16-lane group, lane L of the read receives element L % 4 of the 4-element rows read
-      // by lanes L / 4 + 4 i, i = 0..3.  So lane M reads row key0 + M / 4 at dims 4 (M % 4) ..
-      // + 3 of the tile, and lane (j, r) ends up with keys key0 .. key0 + 3 of dim r; two reads
-      // (key0 = 32 hs + 8 j and + 4) give the 8 keys of the A operand.
-      u32x4 vf[4];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t *vrow = &s_v[buf][(32 * hs + 8 * j + (r >> 2)) * kKStride + 16 * dt + 4 * (r & 3)];
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)vrow);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(vrow + 4 * kKStride));
-        const u32x2 a = __builtin_bit_cast(u32x2, lo), c = __builtin_bit_cast(u32x2, hi);
-        vf[dt] = u32x4{a[0], a[1], c[0], c[1]};
-      }
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
-        // Each weight is carried as a sum of two BF16 values (hi + lo, ~16 significant bits):
-        // with a single BF16 weight a short context keeps the 2^-9 rounding of its few large
-        // weights.
-        u32x4 ph, pl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f2 w2;
-          w2[0] = pe[sub][hs][2 * e];
-          w2[1] = pe[sub][hs][2 * e + 1];
-          const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, b2));
-          ph[e] = hi;
-          f2 rest;  // exact in FP32: each value minus its own BF16 rounding
-          rest[0] = w2[0] - __builtin_bit_cast(float, hi << 16);
-          rest[1] = w2[1] - __builtin_bit_cast(float, hi & 0xFFFF0000u);
-          pl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, b2));
-        }
-        // O^T += V^T P^T, one 16-dim tile at a time; the denominator rides along as an all-ones
-        // tile (every row of it is the query's sum of the same hi + lo weights).
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          o[sub][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[dt]), as_bf16x8(ph), o[sub][dt], 0, 0, 0);
-          o[sub][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[dt]), as_bf16x8(pl), o[sub][dt], 0, 0, 0);
-        }
-        lsum[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kOnes), as_bf16x8(ph), lsum[sub], 0, 0, 0);
-        lsum[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kOnes), as_bf16x8(pl), lsum[sub], 0, 0, 0);
-      }
-    }
-
-    if (more) stage(c + 1, buf ^ 1, rows);
-    __syncthreads();
+    return any_wide;
   };
-  for (int c = 0; c < n_chunks; c += 2) {
-    step(c, std::integral_constant<int, 0>{});
-    if (c + 1 < n_chunks) step(c + 1, std::integral_constant<int, 1>{});
-  }
+  if (run(std::false_type{})) run(std::true_type{});
 
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub) {

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from gpu_helpers import assert_close, bf16_to_bits, to_gpu_bf16, to_gpu_i32
-from workloads import make_prefill, make_prefill_config
+from workloads import f32_to_bf16_bits, make_prefill, make_prefill_config
 
 pytestmark = pytest.mark.gpu
 NAN = np.uint16(0x7FC0)
@@ -155,6 +155,36 @@ def test_prefill_ignores_stale_slots_and_unused_pages(gpu):
     rk, rv = oracle.prefill_kv_append(k_pool, v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, w.v_new)
     ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos)
     assert_close(out, ref, "stale NaN")
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_prefill_values_past_fp16_range(gpu, out_dtype):
+    """The kernel stages V as FP16; a tile whose keys hold a V magnitude past FP16's largest
+    finite value runs again with BF16 V and hi + lo BF16 weights.  Planted values: 7e4 and -3e5
+    in prompt rows of sequence 0 (appended by the call), -1e30 in a cached prefix slot of
+    sequence 2, and 65280 (the largest BF16 value FP16 holds exactly, so the FP16 path) in
+    sequence 1.  Every output row must match the oracle."""
+    import torch
+
+    w = make_prefill(27, [70, 40, 100], [9, 0, 30])
+    v_new, v_pool = w.v_new.copy(), w.v_pool.copy()
+    r0 = [int(x) for x in w.cu_seqlens]
+    v_new[r0[0] + 5, 0, :4] = f32_to_bf16_bits(np.array([7e4, -3e5, 1.0, 7e4], dtype=np.float32))
+    v_new[r0[0] + 60, 1, 10] = f32_to_bf16_bits(np.array([-3e5], dtype=np.float32))[0]
+    v_new[r0[1] + 20, 3, 7] = f32_to_bf16_bits(np.array([65280.0], dtype=np.float32))[0]
+    pos = 17  # a cached prefix position of sequence 2 (its prompt starts at 30)
+    v_pool[int(w.block_tables[2, pos // 16]), 1, pos % 16, 33] = f32_to_bf16_bits(np.array([-1e30], dtype=np.float32))[0]
+    w.v_new, w.v_pool = v_new, v_pool
+    print(f"[prefill] V past FP16 range, out={out_dtype}", flush=True)
+    d = upload(w)
+    out = run(gpu, d, torch.float32 if out_dtype == "f32" else torch.bfloat16).float().cpu().numpy()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, v_new)
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos)
+    if out_dtype == "bf16":  # the tolerance plus the BF16 store's rounding (2^-8 relative)
+        assert np.all(np.abs(out - ref) <= 2e-3 + (1e-2 + 2.0 ** -8) * np.abs(ref)), "BF16 output"
+    else:
+        assert_close(out, ref, "V past FP16 range")
+    assert np.abs(ref).max() > 1e20  # the planted prefix value reaches the outputs
 
 
 @pytest.mark.parametrize("bad", ["entry", "start", "past_table"])
