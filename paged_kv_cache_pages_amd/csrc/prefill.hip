@@ -129,14 +129,14 @@ __device__ __forceinline__ void store_row4(void *out, int64_t elem, f32x4 v) {
 constexpr int kLdsPages = 256;  // block-table entries kept in LDS (4096 tokens); the rest from HBM
 constexpr float kF16Max = 65504.0f;  // largest finite FP16 value
 
-// kChunk keys per step: 64 (two 32-key halves; 166 VGPRs with kSub = 2, 3 waves per SIMD) or 32
+// kChunk keys per step: 64 (two 32-key halves; 165 VGPRs with kSub = 2, 3 waves per SIMD) or 32
 // (one half; fits 128 VGPRs, so 4 waves per SIMD, at twice the steps and barriers per key).
 template <int kSub, int kChunk, bool kOutBf16>
 __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, int32_t tiles) {
   constexpr int kHalves = kChunk / 32;  // 32-key halves per step
   constexpr int kVecs = kChunk / 32;    // 16-byte K (and V) vectors each thread stages per step
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kChunk * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kChunk * kKStride];  // FP16
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kChunk * kKStride];  // FP16 (BF16 in a second pass)
   __shared__ int32_t s_pages[kLdsPages];
   __shared__ int32_t s_bad[kThreads / 64];
   __shared__ int32_t s_wide[2];  // step index whose staged V holds a value past FP16's range
