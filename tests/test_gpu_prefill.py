@@ -187,6 +187,32 @@ def test_prefill_values_past_fp16_range(gpu, out_dtype):
     assert np.abs(ref).max() > 1e20  # the planted prefix value reaches the outputs
 
 
+@pytest.mark.parametrize("prompts", [16, 8])
+def test_prefill_values_past_fp16_range_every_launch_shape(gpu, prompts):
+    """The same second pass in the other two launch shapes: 16 prompts of 256 tokens give
+    16 * 8 * 8 = 1024 groups of 32 rows (32-key steps from 4 per compute unit on a 256-CU part),
+    8 prompts 512 (64-key steps).  Half of the prompts carry a V value past FP16's range; sampled
+    rows of every prompt must match the oracle."""
+    import torch
+
+    w = make_prefill(28 + prompts, [256] * prompts, [0] * prompts)
+    v_new = w.v_new.copy()
+    r0 = [int(x) for x in w.cu_seqlens]
+    rng = np.random.default_rng(prompts)
+    for b in range(0, prompts, 2):
+        row, g, dim = int(rng.integers(0, 256)), int(rng.integers(0, 8)), int(rng.integers(0, 64))
+        v_new[r0[b] + row, g, dim] = f32_to_bf16_bits(np.array([-2.5e6 if b % 4 else 9e4], dtype=np.float32))[0]
+    w.v_new = v_new
+    print(f"[prefill] V past FP16 range, {prompts} prompts x 256", flush=True)
+    d = upload(w)
+    out = run(gpu, d, torch.float32).cpu().numpy()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new, v_new)
+    rows = sorted({r0[b] + k for b in range(prompts) for k in (0, 1, 31, 32, 100, 200, 255)})
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos, rows=rows)
+    assert_close(out[rows], ref[rows], f"V past FP16 range, {prompts} prompts")
+    assert np.abs(ref[rows]).max() > 1e3  # the planted values reach the sampled rows
+
+
 @pytest.mark.parametrize("bad", ["entry", "start", "past_table"])
 def test_prefill_invalid_sequence_gets_zeros(gpu, bad):
     import torch
