@@ -266,8 +266,13 @@ pkv_status pkv_validate_decode_host(const int32_t *block_tables, int32_t max_blo
  *
  * pkv_paged_prefill_attention computes, for every row and query head h, the causal attention of
  * q (device bf16[num_tokens][num_q_heads][64]) over positions 0 .. start + i of the sequence read
- * through its block table (KV head h / 4, scale, FP32 online softmax, BF16 products on the matrix
- * cores), written to out (device, FP32 or BF16 [num_tokens][num_q_heads][64]).  The prompt's own
+ * through its block table (KV head h / 4, scale, FP32 online softmax), written to out (device,
+ * FP32 or BF16 [num_tokens][num_q_heads][64]).  Both products run on the matrix cores with FP32
+ * accumulation: q.k on the BF16 inputs (exact products); p.v with V converted to FP16 (exact for
+ * every BF16 value up to 65280) and each weight rounded to FP16 (11 significant bits, nearest
+ * even), the denominator summing the same rounded weights.  A tile whose keys hold a V magnitude
+ * above 65504 (or an infinity) is recomputed with BF16 V and each weight as two BF16 terms (about
+ * 16 significant bits).  The prompt's own
  * rows must already be in the pool (call the append first, on the same stream).  When start < 0,
  * start + length > 16 * max_blocks_per_seq or any of the sequence's first
  * ceil((start + length) / 16) entries is outside [0, num_pages), all its rows get zeros.  Slots
