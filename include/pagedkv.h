@@ -272,12 +272,12 @@ pkv_status pkv_validate_decode_host(const int32_t *block_tables, int32_t max_blo
  * every BF16 value up to 65280) and each weight rounded to FP16 (11 significant bits, nearest
  * even), the denominator summing the same rounded weights.  A tile whose keys hold a V magnitude
  * above 65504 (or an infinity) is recomputed with BF16 V and each weight as two BF16 terms (about
- * 16 significant bits).  The prompt's own
- * rows must already be in the pool (call the append first, on the same stream).  When start < 0,
- * start + length > 16 * max_blocks_per_seq or any of the sequence's first
- * ceil((start + length) / 16) entries is outside [0, num_pages), all its rows get zeros.  Slots
- * past the last prompt position are never read.  The prompt's own K/V rows must be finite: a
- * NaN in row i can reach earlier rows of the same 32-key step through a zero weight.
+ * 16 significant bits).  The prompt's own rows must already be in the pool (call the append
+ * first, on the same stream).  When start < 0, start + length > 16 * max_blocks_per_seq or any of
+ * the sequence's first ceil((start + length) / 16) entries is outside [0, num_pages), all its rows
+ * get zeros.  Slots past the last prompt position are never read.  The prompt's own K/V rows
+ * must be finite: a NaN in row i can reach earlier rows of the same 32-key step through a zero
+ * weight.
  *
  * Both calls: NULL, shape (negative sizes, num_tokens < 0, max_prompt_len < 0, bad scale or
  * dtype), unsupported geometry and alignment are reported before launching; nothing is launched
