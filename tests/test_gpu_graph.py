@@ -1,4 +1,5 @@
-"""The decode step (append + attention, split and unsplit) captured in a HIP graph and replayed.
+"""The decode step (append + attention, split and unsplit) and the prefill step (append +
+causal attention) captured in a HIP graph and replayed.
 
 Each replay is checked against the eager result, with eager work and synchronisations between
 replays, as graph-replay bugs can show only after the first replay.
@@ -8,8 +9,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import assert_close, bf16_to_bits, upload
-from workloads import make_custom
+from gpu_helpers import assert_close, bf16_to_bits, to_gpu_bf16, to_gpu_i32, upload
+from workloads import f32_to_bf16_bits, make_custom, make_prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -57,3 +58,60 @@ def test_graph_replay_matches_eager(gpu, partition_pages):
         assert np.array_equal(out_graph.cpu().numpy(), eager), f"replay {replay}"
         assert np.array_equal(bf16_to_bits(d["k_pool"]), rk), f"replay {replay} K pool"
         assert np.array_equal(bf16_to_bits(d["v_pool"]), rv), f"replay {replay} V pool"
+
+
+@pytest.mark.parametrize("wide", [False, True])
+def test_prefill_graph_replay_matches_eager(gpu, wide):
+    """Prefill append + attention captured once and replayed: every replay equals the eager run
+    bit for bit (pools and output).  `wide` plants a V value past FP16's range, so the attention
+    takes its BF16 second pass inside the graph too."""
+    import torch
+
+    lens, starts = [200, 37, 96, 1], [0, 40, 300, 7]
+    w = make_prefill(55, lens, starts)
+    if wide:
+        v_new = w.v_new.copy()
+        v_new[int(w.cu_seqlens[2]) + 10, 3, 5] = f32_to_bf16_bits(np.array([3e5], dtype=np.float32))[0]
+        w.v_new = v_new
+    print(f"[graph] prefill lens={lens} starts={starts} wide={wide}", flush=True)
+    kp, vp = to_gpu_bf16(w.k_pool), to_gpu_bf16(w.v_pool)
+    k0, v0 = kp.clone(), vp.clone()
+    bt, cu, st = to_gpu_i32(w.block_tables), to_gpu_i32(w.cu_seqlens), to_gpu_i32(w.start_pos)
+    q, kn, vn = to_gpu_bf16(w.q), to_gpu_bf16(w.k_new), to_gpu_bf16(w.v_new)
+    mpl = max(lens)
+    out_eager = torch.empty((w.tokens, 32, 64), dtype=torch.float32, device="cuda")
+    out_graph = torch.empty_like(out_eager)
+
+    def step(out):
+        gpu.prefill_kv_append(kp, vp, bt, cu, st, kn, vn, max_prompt_len=mpl)
+        gpu.paged_prefill_attention(q, kp, vp, bt, cu, st, out, max_prompt_len=mpl)
+
+    step(out_eager)
+    torch.cuda.synchronize()
+    eager = out_eager.cpu().numpy()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new,
+                                      w.v_new)
+    assert_close(eager, oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos),
+                 "eager prefill")
+
+    kp.copy_(k0)
+    vp.copy_(v0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(out_graph)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(out_graph)
+    for replay in range(4):
+        kp.copy_(k0)
+        vp.copy_(v0)
+        out_graph.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out_graph.cpu().numpy(), eager), f"replay {replay}"
+        assert np.array_equal(bf16_to_bits(kp), rk), f"replay {replay} K pool"
+        assert np.array_equal(bf16_to_bits(vp), rv), f"replay {replay} V pool"
