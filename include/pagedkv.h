@@ -270,19 +270,23 @@ pkv_status pkv_validate_decode_host(const int32_t *block_tables, int32_t max_blo
  * FP32 or BF16 [num_tokens][num_q_heads][64]).  Both products run on the matrix cores with FP32
  * accumulation: q.k on the BF16 inputs (exact products); p.v with V converted to FP16 (exact for
  * every BF16 value up to 65280) and each weight rounded to FP16 (11 significant bits, nearest
- * even), the denominator summing the same rounded weights.  A tile whose keys hold a V magnitude
- * above 65504 (or an infinity) is recomputed with BF16 V and each weight as two BF16 terms (about
- * 16 significant bits).  The prompt's own rows must already be in the pool (call the append
- * first, on the same stream).  When start < 0, start + length > 16 * max_blocks_per_seq or any of
- * the sequence's first ceil((start + length) / 16) entries is outside [0, num_pages), all its rows
- * get zeros.  Slots past the last prompt position are never read.  The prompt's own K/V rows
- * must be finite: a NaN in row i can reach earlier rows of the same 32-key step through a zero
- * weight.
+ * even), the denominator summing the same rounded weights.  A query tile whose keys hold a finite
+ * V magnitude above 65504 is recomputed with BF16 V and each weight as two BF16 terms (about 16
+ * significant bits, not exact).  The prompt's own rows must already be in the pool (call the
+ * append first, on the same stream).  When start < 0, start + length > 16 * max_blocks_per_seq or
+ * any of the sequence's first ceil((start + length) / 16) entries is outside [0, num_pages), all
+ * its rows get zeros.  Slots past the last prompt position are never read.
+ * Precondition: the prompt's own K and V rows are finite.  The kernel multiplies a causally masked
+ * (later) key's V row by weight 0, so an infinity or NaN in prompt row i reaches the earlier rows of
+ * the same query tile (16 or 32 rows), which the definition would leave finite.  Values in the
+ * cached prefix (positions < start) are visible to every row and carry no such caveat.
  *
  * Both calls: NULL, shape (negative sizes, num_tokens < 0, max_prompt_len < 0, bad scale or
  * dtype), unsupported geometry and alignment are reported before launching; nothing is launched
  * when batch, num_tokens or max_prompt_len is 0.  PKV_DEBUG_VALIDATE=1 also runs
- * pkv_validate_prefill_host on copies of the tables, cu_seqlens and start_pos.
+ * pkv_validate_prefill_host on copies of the tables, cu_seqlens and start_pos, and checks the
+ * finiteness precondition with pkv_validate_finite_rows_host: the append on copies of k_new and
+ * v_new, the attention on copies of the prompt rows' pool slots.
  */
 pkv_status pkv_prefill_kv_append(const pkv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
                                  const int32_t *cu_seqlens, const int32_t *start_pos, const void *k_new,
@@ -302,6 +306,12 @@ pkv_status pkv_validate_prefill_host(const int32_t *block_tables, int32_t max_bl
                                      const int32_t *cu_seqlens, const int32_t *start_pos, int32_t batch,
                                      int32_t num_tokens, int32_t max_prompt_len, int32_t num_pages,
                                      int32_t *bad_row);
+
+/* Host-side check (host pointer) that every value of num_rows packed BF16 rows of row_elems
+ * values each is finite (exponent field not all ones).  PKV_ERR_VALIDATION with *bad_row = the
+ * first row holding an infinity or NaN; PKV_OK and *bad_row = -1 otherwise; PKV_ERR_SHAPE for
+ * num_rows < 0 or row_elems <= 0. */
+pkv_status pkv_validate_finite_rows_host(const uint16_t *rows, int32_t num_rows, int32_t row_elems, int32_t *bad_row);
 
 /*
  * Host page allocator with admission credits (plain C++, no GPU; step a0 of a decode loop:

@@ -26,9 +26,11 @@ from ._binding import (  # noqa: F401
     paged_prefill_attention,
     plan_partition_pages,
     prefill_kv_append,
+    release_cached_workspaces,
     require_library,
     rope_kv_append,
     validate_append_host,
     validate_decode_host,
+    validate_finite_rows_host,
     validate_prefill_host,
 )

@@ -89,6 +89,7 @@ SIGNATURES = {
     ),
     "pkv_validate_prefill_host": (
         ctypes.c_int, [_vp, _c_int32, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _vp]),
+    "pkv_validate_finite_rows_host": (ctypes.c_int, [_vp, _c_int32, _c_int32, _vp]),
     "pkv_alloc_create": (ctypes.c_int, [_c_int32, _c_int32, _c_int32, _vp, _c_int32, ctypes.POINTER(_vp)]),
     "pkv_alloc_destroy": (None, [_vp]),
     "pkv_alloc_submit": (ctypes.c_int, [_vp, ctypes.c_int64, _c_int32, _c_int32]),
@@ -214,19 +215,43 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, max_blocks_per_seq: int
 
 
 def _cached_workspace(nbytes: int, device, stream):
-    """A workspace tensor kept per (device, stream) and grown on demand.  Calls on one stream are
-    ordered, so reusing its workspace is safe; other streams get their own.  The tensor is
-    allocated on the stream that uses it, so when a larger one replaces it, torch's allocator
-    hands the old memory out again only to later work on that same stream."""
+    """A workspace tensor kept per (device, stream) and grown on demand (at least doubling, so a
+    stream holds at most about twice its largest request).  Calls on one stream are ordered, so
+    reusing its workspace is safe; other streams get their own.  A workspace that a larger one
+    replaces is retired, not freed: a HIP graph captured with it may still be replayed.  Cached and
+    retired workspaces live until ``release_cached_workspaces()``."""
     torch = _torch()
     s = torch.cuda.current_stream(device) if stream is None else stream
     key = (device.index, s.cuda_stream)
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        with torch.cuda.stream(s):
-            ws = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+    with _lock:
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < nbytes:
+            size = max(nbytes, 1 << 16, 2 * ws.numel() if ws is not None else 0)
+            with torch.cuda.stream(s):
+                new = torch.empty(size, dtype=torch.uint8, device=device)
+            if ws is not None:
+                _retired_workspaces.append(ws)
+            _workspaces[key] = ws = new
     return ws
+
+
+_retired_workspaces = []
+
+
+def release_cached_workspaces() -> int:
+    """Free the workspaces the calls without an explicit ``workspace`` cached (per device and
+    stream), after waiting for the device.  The caller guarantees that no HIP graph captured with
+    one of them is replayed afterwards.  Returns the bytes released."""
+    torch = _torch()
+    with _lock:
+        held = list(_workspaces.values()) + _retired_workspaces
+        freed = sum(int(t.numel()) for t in held)
+        _workspaces.clear()
+        _retired_workspaces.clear()
+    if held and torch.cuda.is_available():
+        torch.cuda.synchronize()
+    del held
+    return freed
 
 
 # ---------------------------------------------------------------------------------------------
@@ -299,7 +324,9 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=No
     ``out_dtype`` is torch.bfloat16 (default) or torch.float32; ``scale`` defaults to
     1/sqrt(head_dim).  ``partition_pages`` <= 0 lets the library plan the context split (with
     ``max_context``, the longest context if the caller knows it, a batch that fits one partition
-    is not split); when no workspace is passed, a torch buffer cached per (device, stream) is used.
+    is not split); when no workspace is passed, a torch buffer cached per (device, stream) is used
+    (it stays allocated until ``release_cached_workspaces()``, so a HIP graph captured with it
+    stays valid until then; passing an explicit workspace keeps its lifetime in the caller's hands).
     """
     torch = _torch()
     _dev_tensor("q", q, torch.bfloat16, 3)
@@ -345,7 +372,8 @@ def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, out=No
 
 def decode_step(q, k_pool, v_pool, block_tables, positions, k_new, v_new, out=None, *, out_dtype=None, scale=None,
                 partition_pages: int = 0, max_context: int | None = None, workspace=None, stream=None):
-    """kv_append then decode attention over positions + 1 tokens, in one launch; returns out."""
+    """kv_append then decode attention over positions + 1 tokens, in one launch; returns out.
+    Partition planning and the workspace work as in ``paged_decode_attention``."""
     torch = _torch()
     _dev_tensor("q", q, torch.bfloat16, 3)
     _dev_tensor("k_pool", k_pool, torch.bfloat16, 4)
@@ -400,7 +428,7 @@ class PreparedDecodeStep:
     arguments straight to the library, on ``stream`` if one was given, else on the stream current
     at the call (so the step can be captured into a graph).  The tensors are kept alive by this
     object; their contents (q, block_tables, positions, k_new, v_new, the pools) are read at
-    launch time."""
+    launch time.  A workspace it allocates itself is recorded on every stream it launches on."""
 
     def __init__(self, q, k_pool, v_pool, block_tables, positions, k_new, v_new, out, *, scale=None,
                  partition_pages: int = 0, max_context: int | None = None, workspace=None, stream=None):
@@ -430,9 +458,13 @@ class PreparedDecodeStep:
             pp = plan_partition_pages(batch, hkv, max_blocks, cu_count(q.device), max_context)
         need = decode_workspace_bytes(batch, hq, max_blocks, pp)
         ws_ptr, ws_bytes = None, 0
+        self._own_ws = None
         if need > 0:
             if workspace is None:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+                # allocated on the stream current now; launches on any other stream are recorded
+                # on it, so torch does not hand the memory out again while they may still run
+                self._own_ws = (workspace, {torch.cuda.current_stream(q.device).cuda_stream})
             _dev_tensor("workspace", workspace, workspace.dtype)
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
             if ws_bytes < need:
@@ -457,6 +489,10 @@ class PreparedDecodeStep:
 
     def __call__(self):
         sh = self._stream if self._stream is not None else self._current()
+        if self._own_ws is not None and sh not in self._own_ws[1]:
+            torch = _torch()
+            self._own_ws[0].record_stream(torch.cuda.ExternalStream(sh, device=self._device))
+            self._own_ws[1].add(sh)
         st = self._fn(*self._args, sh)
         if st != PKV_OK:
             raise PagedKVError("pkv_decode_step", st)
@@ -539,6 +575,19 @@ def validate_prefill_host(block_tables, cu_seqlens, start_pos, num_tokens: int, 
         bt.ctypes.data, bt.shape[1] if bt.ndim == 2 else 0, cu.ctypes.data, sp.ctypes.data, sp.shape[0], num_tokens,
         max_prompt_len, num_pages, ctypes.byref(bad),
     )
+    return int(st), int(bad.value)
+
+
+def validate_finite_rows_host(rows):
+    """Host-side finiteness check of BF16 bit patterns (numpy uint16, first axis = rows):
+    (status, first bad row)."""
+    import numpy as np
+
+    a = np.ascontiguousarray(rows, dtype=np.uint16)
+    n = a.shape[0] if a.ndim else 0
+    elems = int(np.prod(a.shape[1:])) if a.ndim > 1 else 1
+    bad = ctypes.c_int32(-2)
+    st = library().pkv_validate_finite_rows_host(a.ctypes.data, n, elems, ctypes.byref(bad))
     return int(st), int(bad.value)
 
 

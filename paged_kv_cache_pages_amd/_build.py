@@ -19,8 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
-# A plain C++ client of the C ABI (no Python, no PyTorch), used by a GPU test.
-CLIENT_PATH = os.path.join(LIB_DIR, "pkv_abi_client")
+# A plain C++ client of the C ABI (no Python, no PyTorch): test code, built beside its source for
+# a GPU test, never part of the library.
+CLIENT_SRC = os.path.join(ROOT, "tests", "host", "abi_client.cpp")
+CLIENT_PATH = os.path.join(ROOT, "tests", "host", "pkv_abi_client")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_SOURCES = ["pagedkv_api.hip", "kv_append.hip", "paged_attention.hip", "rope_append.hip", "prefill.hip"]
@@ -83,12 +85,13 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
-    client_tmp = CLIENT_PATH + ".tmp"
-    _run(["g++", "-O2", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-I", INCLUDE,
-          os.path.join(CSRC, "abi_client.cpp"), "-o", client_tmp, "-L", LIB_DIR, "-lpagedkv",
-          "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(ROCM, "lib")],
-         verbose)
-    os.replace(client_tmp, CLIENT_PATH)
+    if os.path.exists(CLIENT_SRC):  # a source tree shipped without tests/ has no client
+        client_tmp = CLIENT_PATH + ".tmp"
+        _run(["g++", "-O2", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
+              "-I", INCLUDE, CLIENT_SRC, "-o", client_tmp, "-L", LIB_DIR, "-lpagedkv", "-L", os.path.join(ROCM, "lib"),
+              "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../paged_kv_cache_pages_amd/lib",
+              "-Wl,-rpath," + os.path.join(ROCM, "lib")], verbose)
+        os.replace(client_tmp, CLIENT_PATH)
     return LIB_PATH
 
 

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <vector>
 
@@ -322,9 +323,67 @@ extern "C" pkv_status pkv_decode_step(const pkv_pool *pool, const void *q, const
 
 namespace {
 
+pkv_status copy_bytes_to_host(void *dst, const void *src, size_t n, hipStream_t stream) {
+  if (n == 0) return PKV_OK;
+  if (hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToHost, stream) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+// Debug validation of the prompt rows' values (after the table / bounds checks passed): every K
+// and V value of every sequence's prompt rows must be finite, since the attention kernel gives a
+// masked (later) key weight 0 and 0 times an infinity or NaN would reach earlier rows of the same
+// query tile.  The append checks k_new / v_new; the attention checks the same rows in the pool
+// (where the append put them), copied page by page through the table.
+pkv_status check_prompt_rows_finite(const pkv_pool *pool, const std::vector<int32_t> &bt, int32_t max_blocks,
+                                    const std::vector<int32_t> &cu, const std::vector<int32_t> &st, int32_t batch,
+                                    const void *k_new, const void *v_new, hipStream_t s) {
+  const int32_t hkv = pool->num_kv_heads;
+  const size_t row_elems = (size_t)hkv * pkv::kHeadDim;
+  if (k_new) {
+    const int32_t r0 = cu[0], r1 = cu[batch];  // validated: non-decreasing, inside [0, num_tokens]
+    std::vector<uint16_t> k((size_t)(r1 - r0) * row_elems), v(k.size());
+    const size_t off = (size_t)r0 * row_elems;
+    pkv_status r = copy_bytes_to_host(k.data(), static_cast<const uint16_t *>(k_new) + off, k.size() * 2, s);
+    if (r == PKV_OK) r = copy_bytes_to_host(v.data(), static_cast<const uint16_t *>(v_new) + off, v.size() * 2, s);
+    if (r != PKV_OK) return r;
+    if (hipStreamSynchronize(s) != hipSuccess) return PKV_ERR_HIP;
+    r = pkv_validate_finite_rows_host(k.data(), r1 - r0, (int32_t)row_elems, nullptr);
+    if (r == PKV_OK) r = pkv_validate_finite_rows_host(v.data(), r1 - r0, (int32_t)row_elems, nullptr);
+    return r;
+  }
+  const size_t page_elems = row_elems * pkv::kBlock;
+  std::vector<uint16_t> kp(page_elems), vp(page_elems);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = cu[b + 1] - cu[b], start = st[b];
+    for (int64_t pos0 = start; pos0 < start + n;) {
+      const int64_t blk = pos0 / pkv::kBlock;
+      const int64_t pos1 = std::min<int64_t>(start + n, (blk + 1) * pkv::kBlock);  // this page's prompt slots
+      const int32_t page = bt[(size_t)b * max_blocks + blk];
+      pkv_status r = copy_bytes_to_host(kp.data(), static_cast<const uint16_t *>(pool->k_pool) + page * page_elems,
+                                        page_elems * 2, s);
+      if (r == PKV_OK)
+        r = copy_bytes_to_host(vp.data(), static_cast<const uint16_t *>(pool->v_pool) + page * page_elems,
+                               page_elems * 2, s);
+      if (r != PKV_OK) return r;
+      if (hipStreamSynchronize(s) != hipSuccess) return PKV_ERR_HIP;
+      const int32_t s0 = (int32_t)(pos0 % pkv::kBlock), count = (int32_t)(pos1 - pos0);
+      for (int32_t g = 0; g < hkv && r == PKV_OK; ++g) {
+        const size_t first = ((size_t)g * pkv::kBlock + s0) * pkv::kHeadDim;
+        r = pkv_validate_finite_rows_host(kp.data() + first, count, pkv::kHeadDim, nullptr);
+        if (r == PKV_OK) r = pkv_validate_finite_rows_host(vp.data() + first, count, pkv::kHeadDim, nullptr);
+      }
+      if (r != PKV_OK) return r;
+      pos0 = pos1;
+    }
+  }
+  return PKV_OK;
+}
+
+// Synchronous checks shared by both prefill calls.  `append` selects which copy of the prompt
+// rows debug validation checks for finite values: k_new / v_new (append) or the pool (attention).
 pkv_status prefill_checks(const pkv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
                           const int32_t *cu_seqlens, const int32_t *start_pos, int32_t batch, int32_t num_tokens,
-                          int32_t max_prompt_len, hipStream_t s) {
+                          int32_t max_prompt_len, bool append, const void *k_new, const void *v_new, hipStream_t s) {
   if (!pool) return PKV_ERR_NULL;
   if (batch < 0 || num_tokens < 0 || max_prompt_len < 0 || max_blocks_per_seq <= 0 || pool->num_pages <= 0 ||
       pool->num_kv_heads <= 0)
@@ -342,6 +401,9 @@ pkv_status prefill_checks(const pkv_pool *pool, const int32_t *block_tables, int
     if (r != PKV_OK) return r;
     r = pkv_validate_prefill_host(bt.data(), max_blocks_per_seq, cu.data(), st.data(), batch, num_tokens,
                                   max_prompt_len, pool->num_pages, nullptr);
+    if (r != PKV_OK) return r;
+    r = check_prompt_rows_finite(pool, bt, max_blocks_per_seq, cu, st, batch, append ? k_new : nullptr,
+                                 append ? v_new : nullptr, s);
     if (r != PKV_OK) return r;
   }
   return PKV_OK;
@@ -377,7 +439,7 @@ extern "C" pkv_status pkv_prefill_kv_append(const pkv_pool *pool, const int32_t 
     if (!aligned16(k_new) || !aligned16(v_new)) return PKV_ERR_ALIGNMENT;
   }
   pkv_status st = prefill_checks(pool, block_tables, max_blocks_per_seq, cu_seqlens, start_pos, batch, num_tokens,
-                                 max_prompt_len, s);
+                                 max_prompt_len, true, k_new, v_new, s);
   if (st != PKV_OK || batch == 0 || num_tokens == 0 || max_prompt_len == 0) return st;
   pkv::PrefillParams p =
       prefill_params(pool, block_tables, max_blocks_per_seq, cu_seqlens, start_pos, batch, num_tokens, max_prompt_len);
@@ -401,7 +463,7 @@ extern "C" pkv_status pkv_paged_prefill_attention(const pkv_pool *pool, const vo
     if (!aligned16(q) || !aligned16(out)) return PKV_ERR_ALIGNMENT;
   }
   pkv_status st = prefill_checks(pool, block_tables, max_blocks_per_seq, cu_seqlens, start_pos, batch, num_tokens,
-                                 max_prompt_len, s);
+                                 max_prompt_len, false, nullptr, nullptr, s);
   if (st != PKV_OK || batch == 0 || num_tokens == 0 || max_prompt_len == 0) return st;
   pkv::PrefillParams p =
       prefill_params(pool, block_tables, max_blocks_per_seq, cu_seqlens, start_pos, batch, num_tokens, max_prompt_len);

@@ -24,8 +24,10 @@
 // is staged as FP16, which holds every BF16 value up to 65280 exactly (smaller than 2^-14 in
 // magnitude only to within 2^-25), and the probabilities enter as FP16 (11 significant bits,
 // round to nearest even), so the second product needs one FP16 MFMA per tile.  A tile whose V
-// holds a larger magnitude (or an infinity) is computed again in a second pass with BF16 V and
-// each probability carried as two BF16 terms (hi + lo, about 16 significant bits).
+// holds a larger finite magnitude is computed again in a second pass with BF16 V and each
+// probability carried as two BF16 terms (hi + lo, about 16 significant bits; not exact).  The
+// prompt's own K/V rows must be finite: a causally masked key still enters the second product
+// with weight 0, and 0 times an infinity or NaN reaches the earlier rows of the query tile.
 #include <type_traits>
 
 #include "pkv_internal.h"
@@ -240,7 +242,7 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
     }
   };
   // kWide = false: V is staged as FP16, and a step whose V holds a magnitude past FP16's largest
-  // finite value (or an infinity) marks itself in s_wide (the flag holds the step index, so flags
+  // finite value marks itself in s_wide (the flag holds the step index, so flags
   // of earlier steps never need clearing).  kWide = true: V is staged as BF16.
   auto stage = [&](int c, int buf, Rows &x, auto wide_tag) {
     constexpr bool kWide = decltype(wide_tag)::value;

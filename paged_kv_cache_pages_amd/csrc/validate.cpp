@@ -92,3 +92,22 @@ extern "C" pkv_status pkv_validate_prefill_host(const int32_t *block_tables, int
   }
   return PKV_OK;
 }
+
+// A BF16 value is finite unless its 8 exponent bits are all ones (infinity or NaN).
+extern "C" pkv_status pkv_validate_finite_rows_host(const uint16_t *rows, int32_t num_rows, int32_t row_elems,
+                                                    int32_t *bad_row) {
+  if (bad_row) *bad_row = -1;
+  if (num_rows < 0 || row_elems <= 0) return PKV_ERR_SHAPE;
+  if (num_rows == 0) return PKV_OK;
+  if (!rows) return PKV_ERR_NULL;
+  for (int32_t r = 0; r < num_rows; ++r) {
+    const uint16_t *row = rows + (int64_t)r * row_elems;
+    for (int32_t i = 0; i < row_elems; ++i) {
+      if ((row[i] & 0x7F80u) == 0x7F80u) {
+        if (bad_row) *bad_row = r;
+        return PKV_ERR_VALIDATION;
+      }
+    }
+  }
+  return PKV_OK;
+}

@@ -237,6 +237,27 @@ def test_prefill_validator():
     assert pkv.validate_prefill_host(bt2, [0, 20, 21, 22], [0, 3, 0], 22, 64, 8) == (VALID, 1)  # (page 6, slot 3) twice
 
 
+def test_finite_rows_validator():
+    """Every BF16 pattern whose exponent field is all ones (infinities and NaNs) is rejected; the
+    largest finite values, zeros of both signs and subnormals pass."""
+    from workloads import f32_to_bf16_bits
+
+    rows = f32_to_bf16_bits(np.random.default_rng(0).standard_normal((6, 8, 64)).astype(np.float32))
+    rows[0, 0, :4] = [0x7F7F, 0xFF7F, 0x8000, 0x0001]  # +-max finite, -0, smallest subnormal
+    assert pkv.validate_finite_rows_host(rows) == (OK, -1)
+    for bits in (0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81):  # +inf, -inf, NaNs of both signs
+        bad = rows.copy()
+        bad[4, 7, 63] = bits
+        bad[5, 0, 0] = bits
+        assert pkv.validate_finite_rows_host(bad) == (VALID, 4), hex(bits)
+    assert pkv.validate_finite_rows_host(rows[:0]) == (OK, -1)
+    lib = pkv.library()
+    bad = ctypes.c_int32(-2)
+    assert lib.pkv_validate_finite_rows_host(rows.ctypes.data, -1, 64, ctypes.byref(bad)) == SHAPE
+    assert lib.pkv_validate_finite_rows_host(rows.ctypes.data, 1, 0, ctypes.byref(bad)) == SHAPE
+    assert lib.pkv_validate_finite_rows_host(None, 1, 64, ctypes.byref(bad)) == NULL
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     from paged_kv_cache_pages_amd import _binding
 

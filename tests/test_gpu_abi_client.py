@@ -14,8 +14,7 @@ from workloads import make_config, make_custom
 
 pytestmark = pytest.mark.gpu
 
-CLIENT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "paged_kv_cache_pages_amd", "lib",
-                      "pkv_abi_client")
+CLIENT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "host", "pkv_abi_client")  # built by build()
 
 
 def run_client(tmp_path, w, partition_pages):

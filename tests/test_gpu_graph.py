@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import assert_close, bf16_to_bits, to_gpu_bf16, to_gpu_i32, upload
-from workloads import f32_to_bf16_bits, make_custom, make_prefill
+from gpu_helpers import assert_close, bf16_to_bits, layer_tensors, to_gpu_bf16, to_gpu_i32, upload
+from workloads import f32_to_bf16_bits, make_config, make_custom, make_prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +58,76 @@ def test_graph_replay_matches_eager(gpu, partition_pages):
         assert np.array_equal(out_graph.cpu().numpy(), eager), f"replay {replay}"
         assert np.array_equal(bf16_to_bits(d["k_pool"]), rk), f"replay {replay} K pool"
         assert np.array_equal(bf16_to_bits(d["v_pool"]), rv), f"replay {replay} V pool"
+
+
+@pytest.mark.parametrize("form", ["fused", "two-call"])
+def test_model16_whole_step_graph(gpu, form):
+    """The 16-layer model step (one 128 MiB pool shared by all layers, each layer with its own
+    block table, q and new K/V rows, one workspace shared by every layer) captured as ONE HIP graph
+    in the launch configuration bench.py times (partition plan from the longest context), then
+    replayed three times with the pools restored and the outputs scribbled over in between.  Every
+    replay equals the eager step bit for bit; the eager step's pools equal the oracle's appends
+    applied layer by layer and every layer's output is within tolerance of the oracle."""
+    import torch
+
+    w = make_config("model16")
+    pp = gpu.plan_partition_pages(w.batch, 8, w.max_blocks, max_context=int(w.context_lens.max()))
+    print(f"[graph] model16 form={form} B={w.batch} layers={w.layers} partition_pages={pp}", flush=True)
+    kp, vp = to_gpu_bf16(w.k_pool), to_gpu_bf16(w.v_pool)
+    k0, v0 = kp.clone(), vp.clone()
+    pos, lens = to_gpu_i32(w.positions), to_gpu_i32(w.context_lens)
+    layers = [layer_tensors(w, layer) for layer in range(w.layers)]
+    outs = [torch.empty((w.batch, 32, 64), dtype=torch.float32, device="cuda") for _ in layers]
+    ws = torch.empty(max(16, gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, pp)), dtype=torch.uint8,
+                     device="cuda")
+    if form == "fused":
+        prepared = [gpu.PreparedDecodeStep(t["q"], kp, vp, t["block_tables"], pos, t["k_new"], t["v_new"], o,
+                                           partition_pages=pp, workspace=ws) for t, o in zip(layers, outs)]
+
+        def step():
+            for s in prepared:
+                s()
+    else:
+        def step():  # as bench.py runs it: every layer's append, then every layer's attention
+            for t in layers:
+                gpu.kv_append(kp, vp, t["block_tables"], pos, t["k_new"], t["v_new"])
+            for t, o in zip(layers, outs):
+                gpu.paged_decode_attention(t["q"], kp, vp, t["block_tables"], lens, o, partition_pages=pp,
+                                           workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.cpu().numpy() for o in outs]
+    ek, ev = bf16_to_bits(kp), bf16_to_bits(vp)
+    rk, rv = w.k_pool, w.v_pool
+    for layer in range(w.layers):
+        rk, rv = oracle.kv_append(rk, rv, w.block_tables[layer], w.positions, w.k_new[layer], w.v_new[layer])
+        ref = oracle.paged_decode_attention(w.q[layer], rk, rv, w.block_tables[layer], w.context_lens)
+        assert_close(eager[layer], ref, f"model16 {form} layer {layer}")
+    assert np.array_equal(ek, rk) and np.array_equal(ev, rv)
+
+    kp.copy_(k0)
+    vp.copy_(v0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for replay in range(3):
+        kp.copy_(k0)
+        vp.copy_(v0)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for layer, o in enumerate(outs):
+            assert np.array_equal(o.cpu().numpy(), eager[layer]), f"replay {replay} layer {layer}"
+        assert np.array_equal(bf16_to_bits(kp), ek) and np.array_equal(bf16_to_bits(vp), ev), f"replay {replay} pools"
 
 
 @pytest.mark.parametrize("wide", [False, True])

@@ -393,13 +393,43 @@ def test_debug_validation_rejects_bad_data(gpu):
     torch.cuda.synchronize()
 
 
-def test_long_table_reloads_page_ids(gpu):
-    """A 300-entry table with no split: one wavefront walks more than 64 pages."""
+def test_table_wider_than_one_partition(gpu):
+    """A 300-entry table with partition_pages=300: a partition holds at most 256 pages (four
+    wavefronts with one table entry per lane), so the request is capped and the 282-page context
+    runs as two partitions plus the merge."""
     w = make_custom(seed=33, lengths=[4500, 1100], max_blocks=300)
     d = upload(w)
     out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"], partition_pages=300)
     ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens)
-    assert_close(out.cpu().numpy(), ref, "long table")
+    assert_close(out.cpu().numpy(), ref, "table wider than one partition")
+    split = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"], partition_pages=256)
+    assert np.array_equal(split.cpu().numpy(), out.cpu().numpy())  # the same launch
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_unsplit_partition_of_256_pages(gpu, fused):
+    """The largest unsplit launch: a 256-entry table attended with partition_pages=256, so one
+    workgroup per (sequence, KV head) covers the whole table, each wavefront streams up to 64 pages
+    (one table entry per lane) and no merge runs.  Contexts fill the table exactly, stop one token
+    and one page short of it, and are short."""
+    import torch
+
+    lengths = [4096, 4095, 4081, 2000, 17, 1]
+    w = make_custom(seed=36, lengths=lengths, max_blocks=256)
+    print(f"[parity] unsplit 256-page partition, fused={fused}", flush=True)
+    assert gpu.decode_workspace_bytes(w.batch, 32, 256, 256) == 0  # one partition: no workspace
+    d = upload(w)
+    rk, rv = oracle.kv_append(w.k_pool, w.v_pool, w.block_tables[0], w.positions, w.k_new[0], w.v_new[0])
+    if fused:
+        out = gpu.decode_step(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["positions"], d["k_new"],
+                              d["v_new"], out_dtype=torch.float32, partition_pages=256)
+    else:
+        gpu.kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["positions"], d["k_new"], d["v_new"])
+        out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"], partition_pages=256)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_bits(d["k_pool"]), rk) and np.array_equal(bf16_to_bits(d["v_pool"]), rv)
+    ref = oracle.paged_decode_attention(w.q[0], rk, rv, w.block_tables[0], w.context_lens)
+    assert_close(out.cpu().numpy(), ref, "unsplit 256 pages")
 
 
 def test_other_kv_head_counts(gpu):
