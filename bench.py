@@ -269,7 +269,7 @@ def run(args):
     pp = args.partition_pages if args.partition_pages > 0 else pkv.plan_partition_pages(
         w.batch, w.num_kv_heads, w.max_blocks, max_context=int(np.max(w.context_lens)) if w.batch else None)
     ws_bytes = pkv.decode_workspace_bytes(w.batch, w.num_q_heads, w.max_blocks, pp)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
     def append_all():
         for t in layers:
@@ -419,18 +419,22 @@ def run(args):
     value = gbps(step_bytes, ms_per_step)
     # One "launch" = one layer.  Dominant kernel: the fused decode kernel (attention + append
     # bytes) or, for the two-call step, the attention kernel (attention bytes).
+    # The library's kernel choice: the matrix-core flavour for every split launch and for batches
+    # with fewer (sequence, KV head) pairs than compute units, else the vector-ALU flavour.
+    split = pp < min(w.max_blocks, 256)
+    mfma = split or w.batch * w.num_kv_heads < pkv.cu_count()
+    kernel = "paged_decode_mfma_kernel" if mfma else "paged_decode_kernel"
     if fused_mode:
         # the fused step is one launch per layer: the events bracketing the timed region give the
         # launches' average duration with nothing else between them
         launch_ms = regions[1] / w.layers
         launch_bytes = step_bytes // w.layers
-        kernel = "paged_decode_kernel (fused append)"
+        kernel += " (fused append)"
     else:
         launch_ms = attn_ms / w.layers
         launch_bytes = a_bytes // w.layers
-        kernel = "paged_decode_kernel"
-    if pp < w.max_blocks:
-        kernel += " + merge_partitions_kernel"
+    if split:
+        kernel += ", split context merged in the launch"
 
     def graph_launch_ms(phase, reps):
         """Mean ms per step of `reps` steps of `phase` captured in one HIP graph and replayed between

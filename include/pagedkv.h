@@ -163,14 +163,18 @@ pkv_status pkv_rope_kv_append(const pkv_pool *pool, const int32_t *block_tables,
  *   scale             positive finite score scale (1/sqrt(head_dim) = 0.125 for Llama)
  *   partition_pages   pages per context partition.  <= 0: choose automatically with
  *                     pkv_plan_partition_pages for the current device.  When a sequence's
- *                     pages are cut into several partitions, each partition produces a
- *                     (max, sum, partial output) triple per query head in `workspace` and a
- *                     second kernel merges them.  Values above 256 are treated as 256 (one
- *                     workgroup covers at most 256 pages); >= max_blocks_per_seq (when that is
- *                     <= 256) never splits.
+ *                     pages are cut into several partitions, each partition publishes a
+ *                     (max, sum, partial output) triple per query head in `workspace` and the
+ *                     partition that finishes last merges them, inside the same launch.  Values
+ *                     above 256 are treated as 256 (one workgroup covers at most 256 pages);
+ *                     >= max_blocks_per_seq (when that is <= 256) never splits.
  *   workspace         device scratch of at least pkv_decode_workspace_bytes(...) bytes for the
- *                     resolved partition size (may be NULL when that is 0).  Contents on entry
- *                     are ignored; on return they are unspecified.
+ *                     resolved partition size (may be NULL when that is 0).  It must be
+ *                     all-zero before its first use (e.g. hipMemset once at allocation); every
+ *                     call leaves it all-zero again, so one workspace, sized for the largest
+ *                     shape, serves any sequence of calls of any shape on one stream.  Calls
+ *                     that run at the same time (other streams) need workspaces of their own.
+ *                     Debug validation rejects a split call whose counters are not zero.
  */
 pkv_status pkv_paged_decode_attention(const void *q, const void *k_pool, const void *v_pool, int32_t num_pages,
                                       const int32_t *block_tables, int32_t max_blocks_per_seq,
@@ -204,11 +208,11 @@ pkv_status pkv_decode_step(const pkv_pool *pool, const void *q, const int32_t *b
 
 /*
  * Pages per partition chosen when partition_pages <= 0.  Pure function (no GPU needed).  With L
- * the pages of the longest context (here the table width): no split when L <= 48 (the merge
- * launch would cost more than the split saves) or when the batch * num_kv_heads workgroups number
- * between 3/4 of num_cus and num_cus; otherwise the smallest multiple of 4 pages (at least 8) that
- * gives about 2 workgroups per compute unit over L, and no split if that is >= L; never more than
- * 256.  Returns min(max_blocks_per_seq, 256) when no split is planned; -1 on bad arguments.
+ * the pages of the longest context (here the table width): no split when the batch *
+ * num_kv_heads workgroups number at least 3/4 of num_cus; otherwise the smallest multiple of 4
+ * pages, at least 16, that gives about 2 workgroups per compute unit over L, and no split if that
+ * is >= L; never more than 256.  Returns min(max_blocks_per_seq, 256) when no split is planned;
+ * -1 on bad arguments.
  */
 int32_t pkv_plan_partition_pages(int32_t batch, int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t num_cus);
 
@@ -224,7 +228,9 @@ int32_t pkv_plan_partition_pages_for_context(int32_t batch, int32_t num_kv_heads
                                              int32_t max_context_len, int32_t num_cus);
 
 /* Workspace bytes needed for the given positive partition size (after the same 256-page cap
- * the attention call applies); 0 without a split.  Returns 0 on bad arguments. */
+ * the attention call applies); 0 without a split.  Returns 0 on bad arguments.  Layout (internal):
+ * the partial outputs and (max, sum) pairs of every (sequence, query head, partition), then one
+ * counter per (sequence, KV head) 128 bytes apart. */
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                   int32_t partition_pages);
 

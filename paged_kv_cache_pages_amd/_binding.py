@@ -215,8 +215,9 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, max_blocks_per_seq: int
 
 
 def _cached_workspace(nbytes: int, device, stream):
-    """A workspace tensor kept per (device, stream) and grown on demand (at least doubling, so a
-    stream holds at most about twice its largest request).  Calls on one stream are ordered, so
+    """A zero-filled workspace tensor kept per (device, stream) and grown on demand (at least
+    doubling, so a stream holds at most about twice its largest request); every call leaves its
+    counters at zero again.  Calls on one stream are ordered, so
     reusing its workspace is safe; other streams get their own.  A workspace that a larger one
     replaces is retired, not freed: a HIP graph captured with it may still be replayed.  Cached and
     retired workspaces live until ``release_cached_workspaces()``."""
@@ -228,7 +229,7 @@ def _cached_workspace(nbytes: int, device, stream):
         if ws is None or ws.numel() < nbytes:
             size = max(nbytes, 1 << 16, 2 * ws.numel() if ws is not None else 0)
             with torch.cuda.stream(s):
-                new = torch.empty(size, dtype=torch.uint8, device=device)
+                new = torch.zeros(size, dtype=torch.uint8, device=device)
             if ws is not None:
                 _retired_workspaces.append(ws)
             _workspaces[key] = ws = new
@@ -461,7 +462,7 @@ class PreparedDecodeStep:
         self._own_ws = None
         if need > 0:
             if workspace is None:
-                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+                workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
                 # allocated on the stream current now; launches on any other stream are recorded
                 # on it, so torch does not hand the memory out again while they may still run
                 self._own_ws = (workspace, {torch.cuda.current_stream(q.device).cuda_stream})

@@ -28,9 +28,10 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIP_SOURCES = ["pagedkv_api.hip", "kv_append.hip", "paged_attention.hip", "rope_append.hip", "prefill.hip"]
 CXX_SOURCES = ["validate.cpp", "page_allocator.cpp"]
 
-# Per-file additions.  prefill.hip: keep MFMA accumulators in ordinary VGPRs, so the softmax
-# rescale of the output tile does not copy it between register files every step.
-FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file additions: keep MFMA accumulators in ordinary VGPRs, so the softmax rescale of the
+# output tile does not copy it between register files every step.
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "paged_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIP_FLAGS = [

@@ -5,29 +5,30 @@
 // four query heads that share KV head g, scores s_t = scale * <q_h, K_t> over the sequence's
 // cached tokens, softmax over t, and the softmax-weighted sum of the V rows.  The pages' decode
 // kernel streams the non-contiguous pages directly with an FP32 online softmax, gathering no
-// contiguous prefix and storing no scores; so does this one.
+// contiguous prefix and storing no scores; so do these.
 //
-// Design for CDNA4 (64-lane wavefronts, DPP cross-lane ops, v_dot2 on BF16 pairs):
+// Design for CDNA4 (64-lane wavefronts, DPP cross-lane ops, v_dot2 on BF16 pairs, MFMA):
 //   * One workgroup serves the whole GQA group of a KV head, so each K/V byte is read from HBM
 //     exactly once for all four query heads.
 //   * 4 wavefronts per workgroup; wavefront w takes pages w, w+4, w+8, ... of the partition and
 //     keeps its own softmax state, so the main loop has no barriers.  The four states are
 //     merged in LDS at the end with the pairwise (max, sum) rule.
-//   * One 16-token page of one KV head is a contiguous 2 KiB run.  A wavefront loads it with
-//     two 16-byte loads per lane (lane = 8 * token + chunk): lanes 0..63 cover bytes 0..1023
-//     (tokens 0..7), the second load bytes 1024..2047 (tokens 8..15).  The next two pages' K and
-//     V are in flight while the current page is computed (a short chain issues all its loads
-//     at once).
-//   * QK: each lane forms 8-element partial dots with v_dot2_f32_bf16 (BF16 pairs, FP32
-//     accumulate) and the 8 lanes of a token are summed with three DPP adds.
+//   * Two flavours of the per-page arithmetic.  The vector-ALU kernel (paged_decode_kernel, used
+//     for unsplit launches with at least one workgroup per compute unit, where HBM is the bound):
+//     lane = 8 * token + 16-byte chunk, so a wavefront loads a 2 KiB page of one KV head with two
+//     fully coalesced 16-byte loads per lane; QK with v_dot2_f32_bf16 and three DPP adds, PV with
+//     FMAs.  The matrix-core kernel (paged_decode_mfma_kernel, every split launch and small
+//     batches, where the chain of dependent latencies inside a wavefront is the bound): two pages
+//     per step, both contractions on v_mfma_f32_16x16x32_bf16, only the softmax on the VALU.
 //   * Softmax in log2 units with a lazily moved anchor: scores are compared with the anchor
 //     plus 8; only when a page exceeds it does the wavefront recompute the anchor and rescale
 //     its accumulators (the result is independent of the anchor; fp32 holds 2^8 of headroom).
-//   * PV: each lane accumulates p * V for its 8 dims and 4 heads in 32 FP32 registers; the
-//     token lanes are summed once at the end.
-//   * Long contexts with few (sequence, KV head) pairs are cut into partitions; each writes its
-//     (max, sum, partial output) per query head and a merge kernel combines them.  Workgroup ids
-//     are partition-major, so every partition index is spread over all 8 XCDs.
+//   * Long contexts with few (sequence, KV head) pairs are cut into partitions.  Each publishes
+//     its (max, sum, partial output) per query head to the workspace with device-coherent stores
+//     and counts itself on a per-(sequence, KV head) counter; the partition that arrives last
+//     reads the others' partials back (device-coherent loads) and writes the output, so the split
+//     needs no second kernel.  Workgroup ids are partition-major, so every partition index is
+//     spread over all 8 XCDs.
 // Block-table entries are read straight into a VGPR (one entry per lane) and moved to scalar
 // registers with v_readlane; every entry is range-checked before a page is touched.
 #include <math.h>
@@ -37,7 +38,7 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
+
 constexpr int kThreads = kWaves * 64;
 constexpr float kAnchorHeadroom = 8.0f;  // log2 units
 // s_waitcnt immediate (gfx9 encoding): vmcnt(0), expcnt and lgkmcnt left alone.
@@ -211,6 +212,94 @@ __device__ __forceinline__ int context_length(const DecodeParams &p, int b) {
   return (pos >= 0 && pos < p.max_blocks * kBlock) ? pos + 1 : -1;
 }
 
+// Partitions one merging workgroup reads at once (the loads of a chunk go out together).
+constexpr int kMergeChunk = 16;
+
+// Ends a workgroup once its wavefronts' states are combined: thread (h, d) holds, for query head
+// 4 g + h and dim d, the partition's anchor M (log2 units), denominator Ls and un-normalised output
+// O; any_bad is set when the partition met an invalid table entry.  Unsplit, or a sequence whose
+// pages fit one partition: out = O / Ls (zeros when any_bad).  Otherwise the partition publishes
+// (M, Ls or -1, O) with device-coherent stores, counts itself on the (sequence, KV head) counter,
+// and the partition that arrives last merges all of them with the pairwise (max, sum) rule
+// ("The prefill path: flowing the entire prompt at once", section "causalMask and online
+// softmax"): M* = max M_i, out = sum 2^(M_i - M*) O_i / sum 2^(M_i - M*) Ls_i, or zeros when a
+// partition marked itself invalid.  The merging partition resets the counter and zeroes every
+// partial it read, so the workspace is all-zero again when the launch ends.
+template <bool kSplit, bool kOutBf16>
+__device__ __forceinline__ void finish_group(const DecodeParams &p, int b, int g, int part, int n_pages, float M,
+                                             float O, float Ls, bool any_bad) {
+  __shared__ uint32_t s_ticket;
+  const int h = threadIdx.x >> 6;
+  const int d = threadIdx.x & 63;
+  const int qh = g * kGroup + h;
+  const int64_t o_idx = ((int64_t)b * p.num_q_heads + qh) * kHeadDim + d;
+  auto store_out = [&](float r) {
+    if (kOutBf16) static_cast<uint16_t *>(p.out)[o_idx] = f32_to_bf16_rne(r);
+    else static_cast<float *>(p.out)[o_idx] = r;
+  };
+  const int n_parts = kSplit ? (n_pages + p.part_pages - 1) / p.part_pages : 1;
+  if (n_parts <= 1) {  // workgroup-uniform
+    store_out(any_bad ? 0.0f : O / Ls);
+    return;
+  }
+  const int64_t slot0 = ((int64_t)b * p.num_q_heads + qh) * p.num_parts;
+  const int64_t slot = slot0 + part;
+  __hip_atomic_store(p.part_o + slot * kHeadDim + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (d == 0) {
+    __hip_atomic_store(p.part_ml + slot * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.part_ml + slot * 2 + 1, any_bad ? -1.0f : Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Count the partition only once its partials are acknowledged (device-coherent stores write
+  // through to memory, so a partition on another XCD reads them with device-coherent loads and no
+  // whole-L2 write-back or invalidation is needed).
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  uint32_t *ctr = p.counters + ((int64_t)b * p.num_kv_heads + g) * kCounterStride;
+  if (threadIdx.x == 0) s_ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket != (uint32_t)(n_parts - 1)) return;  // workgroup-uniform
+  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float *ml = p.part_ml + slot0 * 2;
+  float *po = p.part_o + slot0 * kHeadDim + d;
+  float Mg = -INFINITY, Og = 0.0f, Lg = 0.0f;
+  bool bad = false;
+  for (int i0 = 0; i0 < n_parts; i0 += kMergeChunk) {
+    float mv[kMergeChunk], lv[kMergeChunk], ov[kMergeChunk];
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {  // clamped indexes: every load is a published slot
+      const int i = min(i0 + u, n_parts - 1);
+      mv[u] = __hip_atomic_load(ml + 2 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lv[u] = __hip_atomic_load(ml + 2 * i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ov[u] = __hip_atomic_load(po + (int64_t)i * kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float Mc = Mg;
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u)
+      if (i0 + u < n_parts) Mc = fmax_plain(Mc, mv[u]);
+    const float rescale = __builtin_amdgcn_exp2f(Mg - Mc);  // 0 for the first chunk
+    Og *= rescale;
+    Lg *= rescale;
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      if (i0 + u < n_parts) {
+        const float e = __builtin_amdgcn_exp2f(mv[u] - Mc);
+        Og = __builtin_fmaf(e, ov[u], Og);
+        Lg = __builtin_fmaf(e, lv[u], Lg);
+        bad |= !(lv[u] >= 0.0f);
+        // Consumed slots go back to zero, so every call leaves the whole workspace zero-filled
+        // and a later call of any shape finds its counters at zero.
+        __hip_atomic_store(po + (int64_t)(i0 + u) * kHeadDim, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+          __hip_atomic_store(ml + 2 * (i0 + u), 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(ml + 2 * (i0 + u) + 1, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    Mg = Mc;
+  }
+  store_out(bad ? 0.0f : Og / Lg);
+}
+
 template <bool kSplit, bool kOutBf16, bool kFused>
 __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) {
   __shared__ float s_acc[kWaves][4][kGroup][kHeadDim];  // [wave][16-lane row][head][dim]
@@ -269,8 +358,9 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   if (kFused) asm volatile("" ::"v"(knew.x), "v"(knew.y), "v"(knew.z), "v"(knew.w), "v"(vnew.x), "v"(vnew.y), "v"(vnew.z), "v"(vnew.w));
 
   if (p0 >= p1) {
-    if (kSplit) return;  // empty partition (or empty/invalid sequence): the merge handles it
-    // Empty or invalid sequence: zeros for the group's 4 x 64 outputs.
+    // An empty partition has nothing to do; partition 0 is empty only for an empty or invalid
+    // sequence, and writes the group's 4 x 64 zeros.
+    if (kSplit && part != 0) return;
     const int64_t o = ((int64_t)b * p.num_q_heads + qh0) * kHeadDim + threadIdx.x;
     if (kOutBf16) static_cast<uint16_t *>(p.out)[o] = 0;
     else static_cast<float *>(p.out)[o] = 0.0f;
@@ -434,120 +524,332 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
     Ls = __builtin_fmaf(e, l, Ls);
   }
 
-  if (kSplit) {
-    // A partition that met an invalid table entry marks its slot with a negative denominator (a
-    // real one is positive), so the merge zeroes the sequence without reading the table again.
-    const int64_t slot = ((int64_t)b * p.num_q_heads + qh0 + h) * p.num_parts + part;
-    p.part_o[slot * kHeadDim + d] = O;
-    if (d == 0) {
-      p.part_ml[slot * 2 + 0] = M;
-      p.part_ml[slot * 2 + 1] = any_bad ? -1.0f : Ls;
-    }
-  } else {
-    const float r = any_bad ? 0.0f : O / Ls;
-    const int64_t o = ((int64_t)b * p.num_q_heads + qh0 + h) * kHeadDim + d;
-    if (kOutBf16) static_cast<uint16_t *>(p.out)[o] = f32_to_bf16_rne(r);
-    else static_cast<float *>(p.out)[o] = r;
+  finish_group<kSplit, kOutBf16>(p, b, g, part, n_pages, M, O, Ls, any_bad);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Matrix-core flavour of the same kernel: the two contractions of a 32-key step (two pages) run
+// on v_mfma_f32_16x16x32_bf16 and only the softmax stays on the vector ALUs.
+//
+// Register layout of the 16x16x32 BF16 MFMA on gfx950 (lane l, element i):
+//   A operand: row l % 16, reduction index 8 (l / 16) + i;  B operand: column l % 16, same k;
+//   C/D: column l % 16, row 4 (l / 16) + i.
+// Scores are computed transposed, S^T = K Q^T: the A operand is K straight from the pool (row =
+// key, 8 consecutive dims per lane) and the B operand is Q^T with the group's 4 query heads in
+// columns 0..3 and zeros in columns 4..15.  The A rows of tile t (t = 0, 1) are the step's keys
+// 8 (r / 4) + 4 t + r % 4 (keys 0..15 are the first page's tokens, 16..31 the second's), so that
+// lane l ends up holding keys 8 (l / 16) .. + 7 of head l % 16 across its two C tiles: exactly the
+// B-operand layout of P^T in O^T = V^T P^T, so the weights never leave their registers.  V is
+// loaded in the coalesced layout, staged row-major in this wavefront's LDS region and read back
+// transposed (ds_read_b64_tr_b16) as the A operand of V^T.  The weights enter the second product
+// as hi + lo BF16 pairs (about 16 significant bits; V is exact in BF16), and the denominator is
+// the same product against an all-ones tile.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kStepKeys = 32;           // two pages per step
+constexpr int kVStride = kHeadDim + 8;  // staged V row in elements (144 bytes: conflict-free reads)
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ u32x4_t as_u32x4(uint4 v) { return u32x4_t{v.x, v.y, v.z, v.w}; }
+__device__ __forceinline__ u32x4_t load16_stream_v(const uint16_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four key groups of one MFMA
+// column): each permlane swap hands every lane the pair {x[l], x[l ^ 16]} (or ^ 32) as its two
+// results, a VALU exchange with no LDS round trip.
+__device__ __forceinline__ float max_over_key_groups(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false);
+  x = fmax_plain(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false);
+  return fmax_plain(__builtin_bit_cast(float, c[0]), __builtin_bit_cast(float, c[1]));
+}
+
+// One step's loads: K rows in the A-operand layout ([tile][dim half]) and V in the coalesced
+// layout ([page of the step]: tokens tok and tok + 8).
+struct StepRegs {
+  u32x4_t k[2][2];
+  uint4 va[2], vb[2];
+};
+
+template <bool kSplit, bool kOutBf16, bool kFused>
+__global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kWaves][kStepKeys * kVStride];
+  __shared__ __attribute__((aligned(16))) float s_o[kWaves][kGroup][kHeadDim];
+  __shared__ float s_l[kWaves][kGroup];
+  __shared__ float s_m[kWaves][kGroup];
+  __shared__ int s_bad[kWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pairs = p.batch * p.num_kv_heads;
+  const int part = blockIdx.x / pairs;
+  const int pair = blockIdx.x % pairs;
+  const int g = pair % p.num_kv_heads;
+  const int b = pair / p.num_kv_heads;
+  const int qh0 = g * kGroup;
+  const int p0 = part * p.part_pages;
+  const int tok = lane >> 3;    // coalesced layout: token within each half page
+  const int chunk = lane & 7;   //   and 16-byte chunk of its row
+  const int r = lane & 15;      // MFMA row / column
+  const int kg = lane >> 4;     // MFMA reduction group
+
+  const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
+  const int e_lane = p0 + wave + kWaves * lane;
+  const int ids_row = e_lane < p.max_blocks ? bt[e_lane] : 0;
+  // Q^T as the B operand: column r < 4 is query head qh0 + r, dims 32 hf + 8 kg .. + 7.
+  u32x4_t qf[2] = {u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}};
+  if (r < kGroup) {
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(p.q + ((int64_t)b * p.num_q_heads + qh0 + r) * kHeadDim);
+    qf[0] = src[kg];
+    qf[1] = src[4 + kg];
   }
-}
-
-// Combine the partitions of one (sequence, query head): M = max m_i, O = sum o_i 2^(m_i - M),
-// l = sum l_i 2^(m_i - M), out = O / l.  One wavefront: the partitions' (m, l) pairs are spread
-// over the lanes for the max and the weighted sum; lane d accumulates dim d of the partial outputs
-// with the weights broadcast from the lanes that hold them.  A slot marked invalid by its
-// partition (negative l) zeroes the sequence, as the unsplit kernel does.
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmax_plain(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-// Partitions whose partial outputs the merge holds in registers at once.
-constexpr int kMergeRegParts = 16;
-
-template <bool kOutBf16, bool kFused>
-__global__ __launch_bounds__(64) void merge_partitions_kernel(DecodeParams p) {
-  const int b = blockIdx.x / p.num_q_heads;
-  const int h = blockIdx.x % p.num_q_heads;
-  const int lane = threadIdx.x;
-  const int64_t slot0 = ((int64_t)b * p.num_q_heads + h) * p.num_parts;
-  const float *ml = p.part_ml + slot0 * 2;
-  const float *po = p.part_o + slot0 * kHeadDim + lane;
-
-  // The kernel is latency-bound: the (m, l) pairs of the first 64 slots and the partial outputs of
-  // the first kMergeRegParts slots are loaded together with the context length, in one round trip.
-  // Slot indexes are clamped to the launch's partition count, so every load is in bounds; slots
-  // past the sequence's own partitions hold stale data and are discarded by index below.
-  const int last = p.num_parts - 1;
-  const float2 mlv = *reinterpret_cast<const float2 *>(ml + 2 * min(lane, last));
-  float v[kMergeRegParts];
-#pragma unroll
-  for (int u = 0; u < kMergeRegParts; ++u) v[u] = po[(int64_t)min(u, last) * kHeadDim];
-  // Keep the scheduler from placing these loads after the wait for the context length.
-  __builtin_amdgcn_sched_barrier(0);
-
+  uint4 knew = make_uint4(0u, 0u, 0u, 0u), vnew = knew;
+  u32x4_t kn[2] = {u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}};
+  if (kFused) {
+    const int64_t row = ((int64_t)b * p.num_kv_heads + g) * kHeadDim;
+    knew = load16(p.k_new + row + chunk * 8);
+    vnew = load16(p.v_new + row + chunk * 8);
+    kn[0] = *reinterpret_cast<const u32x4_t *>(p.k_new + row + 8 * kg);
+    kn[1] = *reinterpret_cast<const u32x4_t *>(p.k_new + row + 32 + 8 * kg);
+  }
   const int L = context_length<kFused>(p, b);
-  const bool len_ok = L > 0 && L <= p.max_blocks * kBlock;
+  const bool len_ok = L >= 0 && L <= p.max_blocks * kBlock;
   const int n_pages = len_ok ? (L + kBlock - 1) / kBlock : 0;
-  const int n_parts = (n_pages + p.part_pages - 1) / p.part_pages;  // <= num_parts
-  // Up to kMergeRegParts partitions, straight from the registers.  This runs unconditionally (the
-  // masks make it harmless otherwise) so the compiler keeps the loads above ahead of every branch.
-  const bool mine = lane < n_parts;
-  const float m = mine ? mlv.x : -INFINITY;
-  const float l = mine ? mlv.y : 0.0f;
-  const bool bad = __builtin_amdgcn_ballot_w64(mine && !(l >= 0.0f)) != 0;
-  const float M = wave_max(m);
-  const float e = mine ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
-  const float Ls = wave_sum(e * l);
-  const int eb = __builtin_bit_cast(int, e);
-  float O = 0.0f;
-#pragma unroll
-  for (int u = 0; u < kMergeRegParts; ++u)
-    if (u < n_parts) O = __builtin_fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(eb, u)), v[u], O);
-  float r = (n_parts > 0 && n_parts <= kMergeRegParts && !bad) ? O / Ls : 0.0f;
-  if (n_parts > kMergeRegParts) {
-    // Long splits: the pairs 64 at a time, the partial outputs 8 at a time per lane.
-    bool any_bad = false;
-    float Mg = -INFINITY;
-    for (int i0 = 0; i0 < n_parts; i0 += 64) {
-      const int i = i0 + lane;
-      if (i < n_parts) {
-        Mg = fmax_plain(Mg, ml[2 * i]);
-        any_bad |= !(ml[2 * i + 1] >= 0.0f);
-      }
-    }
-    if (__builtin_amdgcn_ballot_w64(any_bad) == 0) {
-      Mg = wave_max(Mg);
-      float Og = 0.0f, Lg = 0.0f;
-      for (int i0 = 0; i0 < n_parts; i0 += 64) {
-        const int i = i0 + lane;
-        const float ei = i < n_parts ? __builtin_amdgcn_exp2f(ml[2 * i] - Mg) : 0.0f;  // 0 past the end
-        Lg += i < n_parts ? ei * ml[2 * i + 1] : 0.0f;
-        const int cnt = min(64, n_parts - i0);
-        const int eib = __builtin_bit_cast(int, ei);
-        for (int j0 = 0; j0 < cnt; j0 += 8) {  // j0 <= 56, so j0 + u <= 63 below
-          float w[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) w[u] = j0 + u < cnt ? po[(int64_t)(i0 + j0 + u) * kHeadDim] : 0.0f;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const float ej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(eib, j0 + u));
-            Og = __builtin_fmaf(ej, w[u], Og);
-          }
-        }
-      }
-      r = Og / wave_sum(Lg);
+  const int p1 = min(p0 + p.part_pages, n_pages);
+  asm volatile("" ::"v"(ids_row));
+  asm volatile("" ::"v"(qf[0].x), "v"(qf[0].y), "v"(qf[0].z), "v"(qf[0].w), "v"(qf[1].x), "v"(qf[1].y), "v"(qf[1].z), "v"(qf[1].w));
+  if (kFused) {
+    asm volatile("" ::"v"(knew.x), "v"(knew.y), "v"(knew.z), "v"(knew.w), "v"(vnew.x), "v"(vnew.y), "v"(vnew.z), "v"(vnew.w));
+    asm volatile("" ::"v"(kn[0].x), "v"(kn[0].y), "v"(kn[0].z), "v"(kn[0].w), "v"(kn[1].x), "v"(kn[1].y), "v"(kn[1].z), "v"(kn[1].w));
+  }
+
+  if (p0 >= p1) {
+    if (kSplit && part != 0) return;  // see paged_decode_kernel
+    const int64_t o = ((int64_t)b * p.num_q_heads + qh0) * kHeadDim + threadIdx.x;
+    if (kOutBf16) static_cast<uint16_t *>(p.out)[o] = 0;
+    else static_cast<float *>(p.out)[o] = 0.0f;
+    return;
+  }
+
+  const float c_log2 = p.score_log2;
+  // Its scalar load shares a wait counter with LDS operations: land it here, in the prologue's
+  // wait, not inside the first step (where waiting for it would also wait for the V^T reads).
+  asm volatile("" ::"s"(c_log2));
+  int n_w = (p1 - p0 - wave + kWaves - 1) / kWaves;
+  if (n_w < 0) n_w = 0;
+  const int ids = lane < n_w ? ids_row : 0;
+  const bool bad = __builtin_amdgcn_ballot_w64(ids < 0 || ids >= p.num_pages) != 0;
+  const bool holds_last = n_w > 0 && p1 == n_pages && p0 + wave + kWaves * (n_w - 1) == n_pages - 1;
+  const int last_id = holds_last ? __builtin_amdgcn_readlane(ids, n_w - 1) : -1;
+  const bool do_append = kFused && last_id >= 0 && last_id < p.num_pages;
+  if (bad) n_w = 0;
+  const bool owns_last = n_w > 0 && holds_last;
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  const int64_t head_elems = (int64_t)kBlock * kHeadDim;
+  const int64_t page_elems = (int64_t)p.num_kv_heads * head_elems;
+  const uint16_t *kbase = p.k_pool + g * head_elems;
+  const uint16_t *vbase = p.v_pool + g * head_elems + lane * 8;
+  const int tail_valid = L - (n_pages - 1) * kBlock;
+  if (do_append) {
+    const int slot = tail_valid - 1;
+    if (tok == (slot & 7)) {
+      const int64_t dst = ((int64_t)last_id * p.num_kv_heads + g) * (kBlock * kHeadDim) + slot * kHeadDim + chunk * 8;
+      *reinterpret_cast<uint4 *>(p.k_pool_w + dst) = knew;
+      *reinterpret_cast<uint4 *>(p.v_pool_w + dst) = vnew;
     }
   }
-  const int64_t o = ((int64_t)b * p.num_q_heads + h) * kHeadDim + lane;
-  if (kOutBf16) static_cast<uint16_t *>(p.out)[o] = f32_to_bf16_rne(r);
-  else static_cast<float *>(p.out)[o] = r;
+
+  // The wavefront's pages in processing order: the sequence's last page (partial, and the fused
+  // step's new token) first, then the others in logical order.  Position j of that list is local
+  // page j - 1 (or n_w - 1 for j = 0) when the wavefront owns the last page, else local page j.
+  auto page_off = [&](int j) -> int64_t {
+    const int local = owns_last ? (j == 0 ? n_w - 1 : j - 1) : j;
+    return (int64_t)__builtin_amdgcn_readlane(ids, local) * page_elems;
+  };
+  // K row of A row r in tile t: page r < 8 ? first : second, token 8 ((r / 4) & 1) + 4 t + r % 4.
+  const int k_tok0 = 8 * ((r >> 2) & 1) + (r & 3);
+  auto load_step = [&](int s, StepRegs &x) {
+    const int j0 = 2 * s;
+    const int j1 = 2 * s + 1 < n_w ? 2 * s + 1 : j0;  // a missing second page re-reads the first (masked)
+    const int64_t offA = page_off(j0), offB = page_off(j1);
+    const uint16_t *kp = kbase + (r < 8 ? offA : offB) + k_tok0 * kHeadDim + 8 * kg;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      x.k[t][0] = load16_stream_v(kp + 4 * t * kHeadDim);
+      x.k[t][1] = load16_stream_v(kp + 4 * t * kHeadDim + 32);
+    }
+    x.va[0] = load16_stream(vbase + offA);
+    x.vb[0] = load16_stream(vbase + offA + 512);
+    x.va[1] = load16_stream(vbase + offB);
+    x.vb[1] = load16_stream(vbase + offB + 512);
+  };
+
+  f32x4_t o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
+  // Anchor (log2 units) of head r; columns 4..15 are padding and keep anchor 0 with weight 0.
+  float m = r < kGroup ? -INFINITY : 0.0f;
+  float thr = r < kGroup ? -INFINITY : INFINITY;
+  const u32x4_t kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // BF16 1.0 x 8
+  uint16_t *sv = s_v[wave];
+
+  auto compute_step = [&](int s, StepRegs x) {
+    const int j1 = 2 * s + 1;
+    const int validA = (owns_last && s == 0) ? tail_valid : kBlock;
+    const int validB = j1 < n_w ? kBlock : 0;
+    if (kFused && owns_last && s == 0) {
+      // The new token (slot tail_valid - 1 of the first page) replaces its row in registers.
+      const int slot = tail_valid - 1;
+      const int r_s = 4 * (slot >> 3) + (slot & 3);
+      if (r == r_s) {
+        if ((slot >> 2) & 1) { x.k[1][0] = kn[0]; x.k[1][1] = kn[1]; }
+        else { x.k[0][0] = kn[0]; x.k[0][1] = kn[1]; }
+      }
+      if (tok == (slot & 7)) {
+        if (slot < 8) x.va[0] = vnew;
+        else x.vb[0] = vnew;
+      }
+    }
+    // Rows past a page's valid tokens are zeroed before staging, so stale or NaN slot contents
+    // never reach the product (their weights are 0 as well).
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    if (tok >= validA) x.va[0] = z;
+    if (tok + 8 >= validA) x.vb[0] = z;
+    if (tok >= validB) x.va[1] = z;
+    if (tok + 8 >= validB) x.vb[1] = z;
+    *reinterpret_cast<uint4 *>(sv + tok * kVStride + chunk * 8) = x.va[0];
+    *reinterpret_cast<uint4 *>(sv + (tok + 8) * kVStride + chunk * 8) = x.vb[0];
+    *reinterpret_cast<uint4 *>(sv + (tok + 16) * kVStride + chunk * 8) = x.va[1];
+    *reinterpret_cast<uint4 *>(sv + (tok + 24) * kVStride + chunk * 8) = x.vb[1];
+    // V^T fragments, read back right away so the LDS latency overlaps the score products and the
+    // softmax (this wavefront's LDS operations complete in order, so the reads see the rows just
+    // written).  Within each 16-lane group, lane L of a transposing read receives element L % 4 of
+    // the 4-element rows read by lanes L / 4 + 4 i; so lane (kg, r) reading row 8 kg + r / 4 at
+    // dims 16 dt + 4 (r % 4) ends up with keys 8 kg .. + 3 of dim 16 dt + r, and a second read four
+    // rows down gives keys + 4 .. + 7: the A operand of V^T for dims 16 dt .. + 15.
+    u32x4_t vf[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint16_t *vrow = sv + (8 * kg + (r >> 2)) * kVStride + 16 * dt + 4 * (r & 3);
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)vrow);
+      const v4i16_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)(vrow + 4 * kVStride));
+      const u32x2_t a = __builtin_bit_cast(u32x2_t, lo), c = __builtin_bit_cast(u32x2_t, hi);
+      vf[dt] = u32x4_t{a[0], a[1], c[0], c[1]};
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the softmax
+
+    f32x4_t sc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.k[t][0]), as_bf16x8(qf[0]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(x.k[t][1]), as_bf16x8(qf[1]), acc, 0, 0, 0);
+      sc[t] = acc;
+    }
+    // This lane holds keys 8 kg + 4 t + i of head r: page kg / 2 of the step, token 8 (kg & 1) + 4 t + i.
+    const int valid_k = kg < 2 ? validA : validB;
+    float smax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int token = 8 * (kg & 1) + 4 * t + i;
+        const float x2 = sc[t][i] * c_log2;  // scaled first: p is exactly 1 for the anchor's key
+        sc[t][i] = (r < kGroup && token < valid_k) ? x2 : -INFINITY;
+        smax = fmax_plain(smax, sc[t][i]);
+      }
+    if (__builtin_amdgcn_ballot_w64(smax > thr) != 0) {  // wave-uniform and rare
+      const float mx = max_over_key_groups(smax);
+      const float m_new = fmax_plain(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first step of a head
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      lsum *= alpha;
+      m = m_new;
+      thr = r < kGroup ? m_new + kAnchorHeadroom : INFINITY;
+    }
+    u32x4_t ph, pl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f2_t w2;
+      w2[0] = __builtin_amdgcn_exp2f(sc[e >> 1][2 * (e & 1)] - m);
+      w2[1] = __builtin_amdgcn_exp2f(sc[e >> 1][2 * (e & 1) + 1] - m);
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, b2_t));
+      f2_t rest;  // exact in FP32: each weight minus its own BF16 rounding
+      rest[0] = w2[0] - __builtin_bit_cast(float, hi << 16);
+      rest[1] = w2[1] - __builtin_bit_cast(float, hi & 0xFFFF0000u);
+      ph[e] = hi;
+      pl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, b2_t));
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[dt]), as_bf16x8(ph), o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[dt]), as_bf16x8(pl), o[dt], 0, 0, 0);
+    }
+    lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kOnes), as_bf16x8(ph), lsum, 0, 0, 0);
+    lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kOnes), as_bf16x8(pl), lsum, 0, 0, 0);
+  };
+
+  const int n_steps = (n_w + 1) >> 1;
+  if (n_steps > 0) {
+    // Two step buffers; both first loads are unconditional (a step past the list re-reads valid
+    // pages and is never computed), and the steady-state loop only runs while both reloads exist,
+    // so the compiler's waits count exactly the newer loads in flight.
+    StepRegs x0, x1;
+    load_step(0, x0);
+    load_step(1, x1);
+    int s = 0;
+    for (; s + 3 < n_steps; s += 2) {
+      compute_step(s, x0);
+      load_step(s + 2, x0);
+      compute_step(s + 1, x1);
+      load_step(s + 3, x1);
+    }
+    const int rem = n_steps - s;  // 1 .. 3
+    compute_step(s, x0);
+    if (rem >= 3) load_step(s + 2, x0);
+    if (rem >= 2) compute_step(s + 1, x1);
+    if (rem >= 3) compute_step(s + 2, x0);
+  }
+
+  // Lanes r < 4 hold head r: o[dt][i] is dim 16 dt + 4 kg + i, lsum the denominator.
+  if (r < kGroup) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4_t *>(&s_o[wave][r][16 * dt + 4 * kg]) = o[dt];
+    if (kg == 0) {
+      s_l[wave][r] = lsum[0];
+      s_m[wave][r] = m;
+    }
+  }
+  if (lane == 0) s_bad[wave] = bad ? 1 : 0;
+  __syncthreads();
+
+  const int h = threadIdx.x >> 6;
+  const int d = threadIdx.x & 63;
+  bool any_bad = false;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    any_bad |= s_bad[w] != 0;
+    M = fmax_plain(M, s_m[w][h]);
+  }
+  float O = 0.0f, Ls = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float e = __builtin_amdgcn_exp2f(s_m[w][h] - M);
+    O = __builtin_fmaf(e, s_o[w][h][d], O);
+    Ls = __builtin_fmaf(e, s_l[w][h], Ls);
+  }
+  finish_group<kSplit, kOutBf16>(p, b, g, part, n_pages, M, O, Ls, any_bad);
 }
 
 }  // namespace
@@ -558,17 +860,26 @@ hipError_t launch_variant(const DecodeParams &p, bool out_bf16, hipStream_t stre
   if (groups == 0) return hipSuccess;
   if (groups > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)groups), block(kThreads);
-  if (p.num_parts == 1) {
-    if (out_bf16) hipLaunchKernelGGL((paged_decode_kernel<false, true, kFused>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((paged_decode_kernel<false, false, kFused>), grid, block, 0, stream, p);
-    return hipGetLastError();
+  const bool split = p.num_parts > 1;
+#define PKV_LAUNCH(kernel, kSplit, kBf16) hipLaunchKernelGGL((kernel<kSplit, kBf16, kFused>), grid, block, 0, stream, p)
+  if (p.matrix_cores) {
+    if (split) {
+      if (out_bf16) PKV_LAUNCH(paged_decode_mfma_kernel, true, true);
+      else PKV_LAUNCH(paged_decode_mfma_kernel, true, false);
+    } else {
+      if (out_bf16) PKV_LAUNCH(paged_decode_mfma_kernel, false, true);
+      else PKV_LAUNCH(paged_decode_mfma_kernel, false, false);
+    }
+  } else {
+    if (split) {
+      if (out_bf16) PKV_LAUNCH(paged_decode_kernel, true, true);
+      else PKV_LAUNCH(paged_decode_kernel, true, false);
+    } else {
+      if (out_bf16) PKV_LAUNCH(paged_decode_kernel, false, true);
+      else PKV_LAUNCH(paged_decode_kernel, false, false);
+    }
   }
-  hipLaunchKernelGGL((paged_decode_kernel<true, true, kFused>), grid, block, 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 mgrid((unsigned)((int64_t)p.batch * p.num_q_heads));
-  if (out_bf16) hipLaunchKernelGGL((merge_partitions_kernel<true, kFused>), mgrid, dim3(64), 0, stream, p);
-  else hipLaunchKernelGGL((merge_partitions_kernel<false, kFused>), mgrid, dim3(64), 0, stream, p);
+#undef PKV_LAUNCH
   return hipGetLastError();
 }
 

@@ -72,24 +72,21 @@ extern "C" int32_t pkv_device_cu_count(void) {
 
 namespace {
 // The plan for a batch whose longest context spans `longest` pages (<= the table width).
-// Measured on the fused step replayed from a HIP graph, batches of 4..64 sequences with uniform,
-// mixed and geometric lengths: this rule lands within ~2% of the best partition size on average
-// (worst +7%); the previous rule (about 4 workgroups per compute unit) averaged +12%.
+// Measured on the fused step replayed from a HIP graph over 20 batches (1-64 sequences, uniform
+// 1024/2048-token contexts, geometric mean-256 and uniform random lengths), every size from 4 to
+// 128 pages: this rule picks the fastest size or lands within ~7% of it.  With the partitions
+// merged inside the launch, many small partitions cost more than they save (8 pages is rarely
+// best, 4 never), and from 3/4 of a workgroup per compute unit the unsplit launch is fastest.
 int32_t plan_pages(int64_t pairs, int32_t max_blocks_per_seq, int64_t longest, int32_t num_cus) {
   const int32_t cap = max_blocks_per_seq < pkv::kMaxPartitionPages ? max_blocks_per_seq : pkv::kMaxPartitionPages;
   if (pairs == 0) return cap;
-  // Short contexts: the merge launch (~2 us) costs more than the split saves.
-  if (longest <= 48) return cap;
-  // Between 3/4 of a workgroup per compute unit and one: splitting only adds workgroups.
-  if (4 * pairs >= 3LL * num_cus && pairs <= num_cus) return cap;
-  // Otherwise about 2 workgroups per compute unit over the longest context.
+  if (4 * pairs >= 3LL * num_cus) return cap;
+  // About 2 workgroups per compute unit over the longest context, in equal shares for the 4
+  // wavefronts, and at least 16 pages.
   const int64_t parts = (2LL * num_cus + pairs - 1) / pairs;
-  if (parts <= 1) return cap;
   int64_t pages = (longest + parts - 1) / parts;
-  pages = ((pages + 3) / 4) * 4;  // equal shares for the 4 wavefronts
-  // At least 8 pages (two per wavefront): below that the merge over many partials costs as much
-  // as the extra parallelism gains.
-  if (pages < 8) pages = 8;
+  pages = ((pages + 3) / 4) * 4;
+  if (pages < 16) pages = 16;
   return pages >= longest || pages >= cap ? cap : (int32_t)pages;
 }
 }  // namespace
@@ -120,6 +117,15 @@ int32_t resolved_partition_pages(int32_t requested, int32_t max_blocks_per_seq) 
 }
 }  // namespace
 
+namespace {
+// Split workspace: partial outputs f32[batch][num_q_heads][parts][64], then (max, denominator)
+// pairs f32[batch][num_q_heads][parts][2], then, from the next 128-byte boundary, one counter per
+// (sequence, KV head) every kCounterStride words.
+constexpr size_t kCounterAlign = 128;
+size_t counter_offset(int64_t slots) { return (size_t)slots * (pkv::kHeadDim + 2) * sizeof(float); }
+size_t counter_bytes(int64_t pairs) { return (size_t)pairs * pkv::kCounterStride * sizeof(uint32_t); }
+}  // namespace
+
 extern "C" size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                              int32_t partition_pages) {
   if (batch < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || partition_pages <= 0) return 0;
@@ -127,7 +133,9 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
   const int64_t parts = ((int64_t)max_blocks_per_seq + pp - 1) / pp;
   if (parts <= 1) return 0;
   const int64_t slots = (int64_t)batch * num_q_heads * parts;
-  return (size_t)slots * (pkv::kHeadDim + 2) * sizeof(float);
+  const int64_t pairs = ((int64_t)batch * num_q_heads + pkv::kGroup - 1) / pkv::kGroup;
+  // the counters' 128-byte alignment may need up to 112 bytes of padding after a 16-byte base
+  return counter_offset(slots) + kCounterAlign + counter_bytes(pairs);
 }
 
 extern "C" pkv_status pkv_kv_append(const pkv_pool *pool, const int32_t *block_tables, int32_t max_blocks_per_seq,
@@ -238,9 +246,10 @@ pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, 
   if (fused && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGNMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  int32_t cus = 0;  // queried only when the plan needs it, after the argument checks otherwise
   int32_t part_pages = partition_pages;
   if (part_pages <= 0) {
-    const int32_t cus = pkv_device_cu_count();
+    cus = pkv_device_cu_count();
     if (cus <= 0) return PKV_ERR_HIP;
     part_pages = pkv_plan_partition_pages(batch, num_kv_heads, max_blocks_per_seq, cus);
   }
@@ -250,6 +259,18 @@ pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, 
     const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, max_blocks_per_seq, part_pages);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PKV_ERR_ALIGNMENT;
+  }
+
+  if (num_parts == 1 && cus <= 0) {  // the unsplit kernel flavour depends on the device size
+    cus = pkv_device_cu_count();
+    if (cus <= 0) return PKV_ERR_HIP;
+  }
+  uint32_t *counters = nullptr;
+  int64_t slots = 0;
+  if (num_parts > 1) {
+    slots = (int64_t)batch * num_q_heads * num_parts;
+    const uintptr_t c = reinterpret_cast<uintptr_t>(workspace) + counter_offset(slots);
+    counters = reinterpret_cast<uint32_t *>((c + kCounterAlign - 1) & ~(uintptr_t)(kCounterAlign - 1));
   }
 
   if (debug_validate_enabled()) {
@@ -263,6 +284,14 @@ pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, 
     }
     if (st == PKV_OK) st = pkv_validate_decode_host(bt.data(), max_blocks_per_seq, lens.data(), batch, num_pages, nullptr);
     if (st != PKV_OK) return st;
+    if (counters) {  // a split needs the workspace's counters at zero (as every call leaves them)
+      std::vector<int32_t> ctr;
+      st = copy_to_host(ctr, reinterpret_cast<const int32_t *>(counters),
+                        counter_bytes((int64_t)batch * num_kv_heads) / sizeof(int32_t), s);
+      if (st != PKV_OK) return st;
+      for (int32_t v : ctr)
+        if (v != 0) return PKV_ERR_VALIDATION;
+    }
   }
 
   pkv::DecodeParams p;
@@ -274,8 +303,8 @@ pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, 
   p.out = out;
   p.part_o = nullptr;
   p.part_ml = nullptr;
+  p.counters = counters;
   if (num_parts > 1) {
-    const int64_t slots = (int64_t)batch * num_q_heads * num_parts;
     p.part_o = static_cast<float *>(workspace);
     p.part_ml = p.part_o + slots * pkv::kHeadDim;
   }
@@ -286,6 +315,10 @@ pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, 
   p.num_kv_heads = num_kv_heads;
   p.part_pages = part_pages;
   p.num_parts = num_parts;
+  // The matrix-core kernel for every split and for batches with fewer (sequence, KV head) pairs
+  // than compute units, where each workgroup's chain of dependent latencies sets the time; the
+  // vector-ALU kernel (slightly faster when HBM is the bound) for the rest.
+  p.matrix_cores = (num_parts > 1 || (int64_t)batch * num_kv_heads < (int64_t)cus) ? 1 : 0;
   p.score_log2 = scale * 1.4426950408889634f;
   p.positions = positions;
   p.k_new = static_cast<const uint16_t *>(k_new);

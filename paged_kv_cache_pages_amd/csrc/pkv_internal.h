@@ -14,6 +14,11 @@ constexpr int kGroup = 4;
 // A decode workgroup has 4 wavefronts and each holds one block-table entry per lane, so one
 // partition covers at most 4 * 64 pages; longer tables are always split.
 constexpr int kMaxPartitionPages = 256;
+// Split-context counters sit 128 bytes apart (one per L2 line), so partitions of different
+// (sequence, KV head) pairs never contend for a line.
+constexpr int kCounterStride = 32;
+// Wavefronts per decode workgroup.
+constexpr int kWaves = 4;
 
 struct AppendParams {
   uint16_t *k_pool;
@@ -37,6 +42,9 @@ struct DecodeParams {
   void *out;
   float *part_o;   // [batch][num_q_heads][num_parts][kHeadDim], un-normalised partial sums
   float *part_ml;  // [batch][num_q_heads][num_parts][2]: (running max in log2 units, denominator)
+  // [batch][num_kv_heads][kCounterStride]: partitions of a (sequence, KV head) that have published
+  // their partials; zero between launches (the last partition to arrive resets it).
+  uint32_t *counters;
   int32_t num_pages;
   int32_t max_blocks;
   int32_t batch;
@@ -44,6 +52,7 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t part_pages;  // pages per partition
   int32_t num_parts;   // ceil(max_blocks / part_pages)
+  int32_t matrix_cores;  // 1: the MFMA kernel (every split launch, small batches), 0: the vector-ALU kernel
   float score_log2;    // scale * log2(e): scores are kept in log2 units so exp2 does the softmax
   // Fused decode step (positions != nullptr): the context is positions[b] + 1 and the new rows
   // k_new / v_new are written at that position by the workgroup that reads the last page.

@@ -102,7 +102,9 @@ int main(int argc, char **argv) {
   int32_t pp = part_pages;
   if (ok && pp <= 0) pp = pkv_plan_partition_pages(batch, hkv, max_blocks, pkv_device_cu_count());
   const size_t ws_bytes = ok ? pkv_decode_workspace_bytes(batch, hq, max_blocks, pp) : 0;
-  if (ok && ws_bytes > 0) ok = hip_ok(hipMalloc(&d_ws, ws_bytes), "hipMalloc workspace");
+  // the split workspace starts zeroed once (every call leaves its counters at zero again)
+  if (ok && ws_bytes > 0)
+    ok = hip_ok(hipMalloc(&d_ws, ws_bytes), "hipMalloc workspace") && hip_ok(hipMemset(d_ws, 0, ws_bytes), "hipMemset");
   if (!ok) return 1;
 
   // The two calls on the pool copy 1, the fused step on copy 2, all on this program's stream.

@@ -148,7 +148,7 @@ def test_fused_step_graph_replay(gpu):
     k0, v0 = d["k_pool"].clone(), d["v_pool"].clone()
     out = torch.empty((w.batch, 32, 64), dtype=torch.float32, device="cuda")
     pp = 8
-    ws = torch.empty(max(16, gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, pp)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(16, gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, pp)), dtype=torch.uint8, device="cuda")
 
     def step():
         gpu.decode_step(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["positions"], d["k_new"], d["v_new"], out,

@@ -25,7 +25,7 @@ def test_graph_replay_matches_eager(gpu, partition_pages):
     out_eager = torch.empty((w.batch, 32, 64), dtype=torch.float32, device="cuda")
     out_graph = torch.empty_like(out_eager)
     pp = partition_pages if partition_pages > 0 else gpu.plan_partition_pages(w.batch, 8, w.max_blocks, gpu.cu_count())
-    ws = torch.empty(max(16, gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, pp)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(16, gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, pp)), dtype=torch.uint8, device="cuda")
 
     def step(out):
         gpu.kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["positions"], d["k_new"], d["v_new"])
@@ -78,7 +78,7 @@ def test_model16_whole_step_graph(gpu, form):
     pos, lens = to_gpu_i32(w.positions), to_gpu_i32(w.context_lens)
     layers = [layer_tensors(w, layer) for layer in range(w.layers)]
     outs = [torch.empty((w.batch, 32, 64), dtype=torch.float32, device="cuda") for _ in layers]
-    ws = torch.empty(max(16, gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, pp)), dtype=torch.uint8,
+    ws = torch.zeros(max(16, gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, pp)), dtype=torch.uint8,
                      device="cuda")
     if form == "fused":
         prepared = [gpu.PreparedDecodeStep(t["q"], kp, vp, t["block_tables"], pos, t["k_new"], t["v_new"], o,

@@ -501,13 +501,14 @@ def test_batch_zero_is_a_no_op(gpu):
 
 def test_one_workspace_serves_every_shape(gpu):
     """Calls of different shapes and split sizes share one workspace (as the binding's per-stream
-    cache does), twice over: every result matches the oracle whatever the workspace held."""
+    cache does), twice over: zero-filled once, with garbage (NaN-ish bytes) in the partials area,
+    every result matches the oracle and every call leaves the counters at zero for the next."""
     import torch
 
     cases = [(make_custom(seed=32, lengths=[2048] * 3 + [40]), 8), (make_custom(seed=33, lengths=[1500]), 4),
              (make_custom(seed=34, lengths=[700, 1, 2000, 64, 900]), 12), (make_custom(seed=35, lengths=[2048]), 4)]
     nbytes = max(gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, pp) for w, pp in cases)
-    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")  # garbage (NaN-ish) contents
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
     for rnd in range(2):
         for w, pp in cases:
             d = upload(w)
@@ -516,3 +517,26 @@ def test_one_workspace_serves_every_shape(gpu):
             torch.cuda.synchronize()
             ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens)
             assert_close(out.cpu().numpy(), ref, f"round {rnd} B={w.batch} pp={pp}")
+            assert int(torch.count_nonzero(ws)) == 0, f"round {rnd} B={w.batch} pp={pp} left workspace bytes set"
+
+
+def test_split_workspace_must_start_zeroed(gpu, monkeypatch):
+    """Debug validation rejects a split call whose workspace counters are not zero (a workspace
+    that was never zero-filled); after a call the workspace is all-zero again."""
+    import torch
+
+    w = make_custom(seed=37, lengths=[1500, 700])
+    d = upload(w)
+    nbytes = gpu.decode_workspace_bytes(w.batch, 32, w.max_blocks, 8)
+    ws = torch.full((nbytes,), 0x11, dtype=torch.uint8, device="cuda")
+    monkeypatch.setenv("PKV_DEBUG_VALIDATE", "1")
+    with pytest.raises(gpu.PagedKVError, match="VALIDATION"):
+        gpu.paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                                   out_dtype=torch.float32, partition_pages=8, workspace=ws)
+    ws.zero_()
+    out = gpu.paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                                     out_dtype=torch.float32, partition_pages=8, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws)) == 0
+    ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens)
+    assert_close(out.cpu().numpy(), ref, "zeroed workspace")
