@@ -63,7 +63,8 @@ typedef enum {
   PKV_ERR_ALIGNMENT = 7,   /* a device buffer is not 16-byte aligned                        */
   PKV_ERR_REJECTED = 8,    /* allocator: the request can never be served (see pkv_alloc_*)  */
   PKV_ERR_STATE = 9,       /* allocator: unknown request id, or an id already queued/active */
-  PKV_ERR_EXHAUSTED = 10   /* allocator: the page would exceed the request's credits        */
+  PKV_ERR_EXHAUSTED = 10,  /* allocator: the page would exceed the request's credits        */
+  PKV_ERR_SCRATCH = 11     /* pkv_decode_step_static: the split exceeds the static scratch  */
 } pkv_status;
 
 typedef enum {
@@ -205,6 +206,26 @@ pkv_status pkv_decode_step(const pkv_pool *pool, const void *q, const int32_t *b
                            const int32_t *positions, const void *k_new, const void *v_new, void *out,
                            pkv_out_dtype out_dtype, int32_t batch, int32_t num_q_heads, float scale,
                            int32_t partition_pages, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * decode_step_static: pkv_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, hosts that forbid hipMalloc).  Same arguments, results
+ * and out-of-range behaviour as pkv_decode_step, without the workspace: a split uses scratch that
+ * the library holds in a static device array of PKV_STATIC_SCRATCH_BYTES per GPU (kept until the
+ * process ends, its address resolved once per device on the first call there).  Allocates
+ * nothing: no hipMalloc/hipFree and no host buffers (so PKV_DEBUG_VALIDATE does not apply here).
+ *   Returns PKV_ERR_SCRATCH when pkv_decode_workspace_bytes(batch, num_q_heads,
+ *   max_blocks_per_seq, resolved partition size) exceeds PKV_STATIC_SCRATCH_BYTES (nothing is
+ *   launched); an unsplit call needs no scratch.
+ *   All calls on one GPU share its array: calls that can run at the same time on one GPU (other
+ *   streams, other threads) race and must not overlap.  The array starts zero-filled and every
+ *   call leaves it zero-filled, which is what a split needs.
+ */
+#define PKV_STATIC_SCRATCH_BYTES (4u << 20)
+pkv_status pkv_decode_step_static(const pkv_pool *pool, const void *q, const int32_t *block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t *positions, const void *k_new,
+                                  const void *v_new, void *out, pkv_out_dtype out_dtype, int32_t batch,
+                                  int32_t num_q_heads, float scale, int32_t partition_pages, void *stream);
 
 /*
  * Pages per partition chosen when partition_pages <= 0.  Pure function (no GPU needed).  With L

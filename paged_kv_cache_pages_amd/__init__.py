@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     PKV_OUT_F32,
     AllocStats,
     PageAllocator,
+    STATIC_SCRATCH_BYTES,
     SIGNATURES,
     STATUS_NAMES,
     PagedKVError,
@@ -19,6 +20,7 @@ from ._binding import (  # noqa: F401
     PreparedDecodeStep,
     cu_count,
     decode_step,
+    decode_step_static,
     decode_workspace_bytes,
     kv_append,
     library,

@@ -29,6 +29,7 @@ STATUS_NAMES = {
     8: "PKV_ERR_REJECTED",
     9: "PKV_ERR_STATE",
     10: "PKV_ERR_EXHAUSTED",
+    11: "PKV_ERR_SCRATCH",
 }
 
 # Every symbol the header declares, with its ctypes signature.
@@ -71,6 +72,11 @@ SIGNATURES = {
         ctypes.c_int,
         [ctypes.POINTER(Pool), _vp, _vp, _c_int32, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int32, _c_int32,
          ctypes.c_float, _c_int32, _vp, _c_size, _vp],
+    ),
+    "pkv_decode_step_static": (
+        ctypes.c_int,
+        [ctypes.POINTER(Pool), _vp, _vp, _c_int32, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int32, _c_int32,
+         ctypes.c_float, _c_int32, _vp],
     ),
     "pkv_plan_partition_pages": (_c_int32, [_c_int32, _c_int32, _c_int32, _c_int32]),
     "pkv_plan_partition_pages_for_context": (_c_int32, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32]),
@@ -419,6 +425,48 @@ def decode_step(q, k_pool, v_pool, block_tables, positions, k_new, v_new, out=No
         float(scale), pp, ws_ptr, ws_bytes, sh,
     )
     _check("pkv_decode_step", st)
+    return out
+
+
+STATIC_SCRATCH_BYTES = 4 << 20  # PKV_STATIC_SCRATCH_BYTES
+
+
+def decode_step_static(q, k_pool, v_pool, block_tables, positions, k_new, v_new, out, *, scale=None,
+                       partition_pages: int = 0, max_context: int | None = None, stream=None):
+    """pkv_decode_step_static: decode_step without a workspace; a split uses the library's static
+    per-GPU scratch (PKV_STATIC_SCRATCH_BYTES), so the call allocates no device memory.  ``out``
+    must be given (bfloat16 or float32 [B][Hq][D]).  Calls that may overlap on one GPU race."""
+    torch = _torch()
+    _dev_tensor("q", q, torch.bfloat16, 3)
+    _dev_tensor("k_pool", k_pool, torch.bfloat16, 4)
+    _dev_tensor("v_pool", v_pool, torch.bfloat16, 4)
+    _dev_tensor("block_tables", block_tables, torch.int32, 2)
+    _dev_tensor("positions", positions, torch.int32, 1)
+    _dev_tensor("k_new", k_new, torch.bfloat16, 3)
+    _dev_tensor("v_new", v_new, torch.bfloat16, 3)
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be a bfloat16 or float32 tensor")
+    _dev_tensor("out", out, out.dtype, 3)
+    batch, hq, dim = q.shape
+    num_pages, hkv, block, _ = k_pool.shape
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != (batch, hq, dim):
+        raise ValueError("inconsistent pool / out shapes")
+    if block_tables.shape[0] != batch or positions.shape[0] != batch:
+        raise ValueError("block_tables / positions batch differs from q")
+    if tuple(k_new.shape) != (batch, hkv, dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new / v_new must be [batch][kv_heads][head_dim]")
+    max_blocks = block_tables.shape[1]
+    scale = 1.0 / float(dim) ** 0.5 if scale is None else float(scale)
+    pp = int(partition_pages)
+    if pp <= 0:
+        pp = plan_partition_pages(batch, hkv, max_blocks, cu_count(q.device), max_context)
+    pool = Pool(k_pool.data_ptr(), v_pool.data_ptr(), num_pages, hkv, dim, block)
+    st = library().pkv_decode_step_static(
+        ctypes.byref(pool), q.data_ptr(), block_tables.data_ptr(), max_blocks, positions.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), out.data_ptr(), PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32, batch, hq,
+        scale, pp, _stream_handle(stream, q.device),
+    )
+    _check("pkv_decode_step_static", st)
     return out
 
 

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "pagedkv.h"
@@ -51,6 +52,7 @@ extern "C" const char *pkv_status_string(pkv_status status) {
     case PKV_ERR_REJECTED: return "request rejected: invalid lengths, or its page credits exceed the whole pool";
     case PKV_ERR_STATE: return "unknown request id, or the id is already queued or active";
     case PKV_ERR_EXHAUSTED: return "the page would exceed the request's admission credits";
+    case PKV_ERR_SCRATCH: return "the split needs more than the library's static scratch (PKV_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -224,6 +226,33 @@ extern "C" pkv_status pkv_rope_kv_append(const pkv_pool *pool, const int32_t *bl
 
 namespace {
 
+// Scratch for pkv_decode_step_static: one array per device, resolved once per device with
+// hipGetSymbolAddress and only ever passed to kernels through that address.  Static storage starts
+// zero-filled, and every decode call leaves its split scratch all-zero again (the partition that
+// merges a split resets its counter and zeroes the partials it read), which is the state a split
+// needs when it starts.
+static __device__ __align__(256) unsigned char scratch[PKV_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // written and read under g_scratch_mutex
+
+pkv_status static_scratch_address(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return PKV_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+namespace {
+
 // Shared by the attention call and the fused decode step.  `positions` != nullptr selects the
 // fused step: the context is positions[b] + 1 and k_new / v_new are appended on the way.
 pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, int32_t num_pages,
@@ -231,7 +260,7 @@ pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, 
                          const int32_t *positions, const void *k_new, const void *v_new, void *out,
                          pkv_out_dtype out_dtype, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, float scale, int32_t partition_pages, void *workspace,
-                         size_t workspace_bytes, void *stream) {
+                         size_t workspace_bytes, void *stream, bool static_scratch = false) {
   const bool fused = positions != nullptr;
   if (batch < 0 || num_pages <= 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0)
     return PKV_ERR_SHAPE;
@@ -257,6 +286,12 @@ pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, 
   const int32_t num_parts = (max_blocks_per_seq + part_pages - 1) / part_pages;
   if (num_parts > 1) {
     const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, max_blocks_per_seq, part_pages);
+    if (static_scratch) {
+      if (need > PKV_STATIC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
+      pkv_status st = static_scratch_address(&workspace);
+      if (st != PKV_OK) return st;
+      workspace_bytes = PKV_STATIC_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PKV_ERR_ALIGNMENT;
   }
@@ -273,7 +308,7 @@ pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, 
     counters = reinterpret_cast<uint32_t *>((c + kCounterAlign - 1) & ~(uintptr_t)(kCounterAlign - 1));
   }
 
-  if (debug_validate_enabled()) {
+  if (!static_scratch && debug_validate_enabled()) {  // the static-scratch entry allocates nothing
     std::vector<int32_t> bt, lens;
     pkv_status st = copy_to_host(bt, block_tables, (size_t)batch * max_blocks_per_seq, s);
     if (st == PKV_OK) st = copy_to_host(lens, fused ? positions : context_lens, (size_t)batch, s);
@@ -352,6 +387,17 @@ extern "C" pkv_status pkv_decode_step(const pkv_pool *pool, const void *q, const
   return decode_common(q, pool->k_pool, pool->v_pool, pool->num_pages, block_tables, max_blocks_per_seq, nullptr,
                        positions, k_new, v_new, out, out_dtype, batch, num_q_heads, pool->num_kv_heads, pool->head_dim,
                        pool->block_size, scale, partition_pages, workspace, workspace_bytes, stream);
+}
+
+extern "C" pkv_status pkv_decode_step_static(const pkv_pool *pool, const void *q, const int32_t *block_tables,
+                                             int32_t max_blocks_per_seq, const int32_t *positions, const void *k_new,
+                                             const void *v_new, void *out, pkv_out_dtype out_dtype, int32_t batch,
+                                             int32_t num_q_heads, float scale, int32_t partition_pages, void *stream) {
+  if (!pool) return PKV_ERR_NULL;
+  if (batch > 0 && !positions) return PKV_ERR_NULL;
+  return decode_common(q, pool->k_pool, pool->v_pool, pool->num_pages, block_tables, max_blocks_per_seq, nullptr,
+                       positions, k_new, v_new, out, out_dtype, batch, num_q_heads, pool->num_kv_heads, pool->head_dim,
+                       pool->block_size, scale, partition_pages, nullptr, 0, stream, /*static_scratch=*/true);
 }
 
 namespace {

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     assert lib.pkv_abi_version() == 1
-    for code in range(11):
+    for code in range(12):
         assert lib.pkv_status_string(code)
     assert b"aligned" in lib.pkv_status_string(ALIGN)
 
@@ -138,6 +138,21 @@ def test_decode_host_checks(lib):
     assert _decode(lib, pp=4) == WS
     assert _decode(lib, pp=4, ws=FAKE, wsb=need - 1) == WS
     assert _decode(lib, pp=4, ws=FAKE + 8, wsb=need) == ALIGN
+
+
+def test_static_scratch_step_host_checks(lib):
+    """pkv_decode_step_static rejects a split larger than its static scratch before touching the
+    device, and checks its arguments like pkv_decode_step."""
+    pool = pkv.Pool(FAKE, FAKE, 64, 8, 64, 16)
+    args = lambda batch, maxb, pp, q=FAKE, pos=FAKE: (ctypes.byref(pool), q, FAKE, maxb, pos, FAKE, FAKE, FAKE, 1,
+                                                       batch, 32, 0.125, pp, None)
+    assert pkv.decode_workspace_bytes(64, 32, 128, 4) > pkv.STATIC_SCRATCH_BYTES
+    assert lib.pkv_decode_step_static(*args(64, 128, 4)) == 11  # PKV_ERR_SCRATCH
+    assert b"static scratch" in lib.pkv_status_string(11)
+    assert lib.pkv_decode_step_static(*args(1, 128, 16, q=None)) == NULL
+    assert lib.pkv_decode_step_static(*args(1, 128, 16, pos=None)) == NULL
+    assert lib.pkv_decode_step_static(*args(0, 128, 16)) == OK
+    assert lib.pkv_decode_step_static(None, *args(1, 128, 16)[1:]) == NULL
 
 
 def test_rope_append_host_checks(lib):
