@@ -33,7 +33,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 METRIC = "paged decode attention GB/s and % of HBM peak; seq-tokens attended/sec"
 ATTN_SOURCE = os.path.join(ROOT, "paged_kv_cache_pages_amd", "csrc", "paged_attention.hip")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_bw256_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_decode_{config}_traffic.md")
 PREFILL_SOURCE = os.path.join(ROOT, "paged_kv_cache_pages_amd", "csrc", "prefill.hip")
 PREFILL_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "paged_prefill_16x512_traffic.md")
 
@@ -92,9 +92,9 @@ def kernel_source_digest(path: str = ATTN_SOURCE) -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def recorded_traffic(tag: str, profile: str = TRAFFIC_PROFILE, source: str = ATTN_SOURCE):
+def recorded_traffic(tag: str, profile: str, source: str = ATTN_SOURCE):
     """Traffic per launch of the ``tag`` kernel from a committed counter summary, or None when the
-    kernel source has changed since the counters were taken."""
+    summary is missing or the kernel source has changed since the counters were taken."""
     if not os.path.exists(profile):
         return None
     text = open(profile).read()
@@ -458,8 +458,9 @@ def run(args):
     reps = max(10, min(K, 100))
     launch_ms_graph = graph_launch_ms(fused_all if fused_mode else attend_all, reps) / w.layers
     achieved = gbps(launch_bytes, launch_ms)
-    traffic = recorded_traffic("fused" if fused_mode else "attention") \
-        if pp >= w.max_blocks and args.config == "bw256" else None
+    # counters are recorded for the partition plan the bench uses by default
+    traffic = recorded_traffic("fused" if fused_mode else "attention", TRAFFIC_PROFILE.format(config=args.config)) \
+        if args.partition_pages <= 0 else None
 
     result = {
         "metric": METRIC,

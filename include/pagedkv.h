@@ -162,6 +162,8 @@ pkv_status pkv_rope_kv_append(const pkv_pool *pool, const int32_t *block_tables,
  *                     0 gives an all-zero output row
  *   out               device, bf16 or f32 [batch][num_q_heads][head_dim] per out_dtype
  *   scale             positive finite score scale (1/sqrt(head_dim) = 0.125 for Llama)
+ *   batch             0 .. 65535 sequences (PKV_ERR_SHAPE above); a partition size giving more
+ *                     than 65535 partitions is PKV_ERR_SHAPE as well
  *   partition_pages   pages per context partition.  <= 0: choose automatically with
  *                     pkv_plan_partition_pages for the current device.  When a sequence's
  *                     pages are cut into several partitions, each partition publishes a

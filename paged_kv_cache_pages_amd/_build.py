@@ -31,7 +31,9 @@ CXX_SOURCES = ["validate.cpp", "page_allocator.cpp"]
 # Per-file additions: keep MFMA accumulators in ordinary VGPRs, so the softmax rescale of the
 # output tile does not copy it between register files every step.
 FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "paged_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "paged_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
+                                      # the decode kernels' 14 leading argument dwords go to SGPRs
+                                      "-mllvm", "-amdgpu-kernarg-preload-count=14"]}
 
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIP_FLAGS = [

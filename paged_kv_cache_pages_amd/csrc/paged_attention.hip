@@ -212,6 +212,29 @@ __device__ __forceinline__ int context_length(const DecodeParams &p, int b) {
   return (pos >= 0 && pos < p.max_blocks * kBlock) ? pos + 1 : -1;
 }
 
+// The arguments the prologue's first loads depend on lead the kernel signature as scalars, so the
+// hardware preloads them into SGPRs before the wavefront starts (the build asks for 14 dwords of
+// preload): the table row, context or position, q and the new row are then requested by the very
+// first instructions instead of behind a kernel-argument load.  The struct follows for the rest.
+#define PKV_PRELOADED_ARGS                                                                           \
+  const int32_t *pre_tables, const int32_t *pre_lens, const uint16_t *pre_q, const uint16_t *pre_k_new, \
+      const uint16_t *pre_v_new, int32_t pre_max_blocks, int32_t pre_kv_heads, int32_t pre_batch,     \
+      int32_t pre_part_pages
+#define PKV_TAKE_PRELOADED_ARGS(p)   \
+  do {                               \
+    (p).block_tables = pre_tables;   \
+    if (kFused) (p).positions = pre_lens; \
+    else (p).context_lens = pre_lens; \
+    (p).q = pre_q;                   \
+    (p).k_new = pre_k_new;           \
+    (p).v_new = pre_v_new;           \
+    (p).max_blocks = pre_max_blocks; \
+    (p).num_kv_heads = pre_kv_heads; \
+    (p).num_q_heads = kGroup * pre_kv_heads; \
+    (p).batch = pre_batch;           \
+    (p).part_pages = pre_part_pages; \
+  } while (0)
+
 // Partitions one merging workgroup reads at once (the loads of a chunk go out together).
 constexpr int kMergeChunk = 16;
 
@@ -301,7 +324,8 @@ __device__ __forceinline__ void finish_group(const DecodeParams &p, int b, int g
 }
 
 template <bool kSplit, bool kOutBf16, bool kFused>
-__global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) void paged_decode_kernel(PKV_PRELOADED_ARGS, DecodeParams p) {
+  PKV_TAKE_PRELOADED_ARGS(p);
   __shared__ float s_acc[kWaves][4][kGroup][kHeadDim];  // [wave][16-lane row][head][dim]
   __shared__ float s_l[kWaves][4][kGroup];
   __shared__ float s_m[kWaves][kGroup];
@@ -313,11 +337,11 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeParams p) 
   // partition as the fast index (and 8 partitions) partition k would always land on XCD k, and the
   // XCD holding every sequence's first partition would do most of the work.  With the (sequence,
   // KV head) pair fast, each partition is spread over all XCDs.
-  const int pairs = p.batch * p.num_kv_heads;
-  const int part = blockIdx.x / pairs;
-  const int pair = blockIdx.x % pairs;
-  const int g = pair % p.num_kv_heads;
-  const int b = pair / p.num_kv_heads;
+  // Grid (KV head, sequence, partition): workgroups are dispatched x-fastest, so the linear order
+  // is partition-major as described above, and no index needs a division.
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int part = blockIdx.z;
   const int qh0 = g * kGroup;  // first query head of the group
 
   const int p0 = part * p.part_pages;
@@ -578,7 +602,8 @@ struct StepRegs {
 };
 
 template <bool kSplit, bool kOutBf16, bool kFused>
-__global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(PKV_PRELOADED_ARGS, DecodeParams p) {
+  PKV_TAKE_PRELOADED_ARGS(p);
   __shared__ __attribute__((aligned(16))) uint16_t s_v[kWaves][kStepKeys * kVStride];
   __shared__ __attribute__((aligned(16))) float s_o[kWaves][kGroup][kHeadDim];
   __shared__ float s_l[kWaves][kGroup];
@@ -587,11 +612,9 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeParam
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int pairs = p.batch * p.num_kv_heads;
-  const int part = blockIdx.x / pairs;
-  const int pair = blockIdx.x % pairs;
-  const int g = pair % p.num_kv_heads;
-  const int b = pair / p.num_kv_heads;
+  const int g = blockIdx.x;  // grid (KV head, sequence, partition), as in paged_decode_kernel
+  const int b = blockIdx.y;
+  const int part = blockIdx.z;
   const int qh0 = g * kGroup;
   const int p0 = part * p.part_pages;
   const int tok = lane >> 3;    // coalesced layout: token within each half page
@@ -800,10 +823,13 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(DecodeParam
   };
 
   const int n_steps = (n_w + 1) >> 1;
-  if (n_steps > 0) {
-    // Two step buffers; both first loads are unconditional (a step past the list re-reads valid
-    // pages and is never computed), and the steady-state loop only runs while both reloads exist,
-    // so the compiler's waits count exactly the newer loads in flight.
+  if (n_steps == 1) {  // one step (short contexts): no second buffer, no loads beyond the pages
+    StepRegs x0;
+    load_step(0, x0);
+    compute_step(0, x0);
+  } else if (n_steps > 1) {
+    // Two step buffers; both first loads are unconditional, and the steady-state loop only runs
+    // while both reloads exist, so the compiler's waits count exactly the newer loads in flight.
     StepRegs x0, x1;
     load_step(0, x0);
     load_step(1, x1);
@@ -858,10 +884,13 @@ template <bool kFused>
 hipError_t launch_variant(const DecodeParams &p, bool out_bf16, hipStream_t stream) {
   const int64_t groups = (int64_t)p.batch * p.num_kv_heads * p.num_parts;
   if (groups == 0) return hipSuccess;
-  if (groups > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)groups), block(kThreads);
+  if (groups > 0x7fffffff || p.batch > 65535 || p.num_parts > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)p.num_kv_heads, (unsigned)p.batch, (unsigned)p.num_parts), block(kThreads);
   const bool split = p.num_parts > 1;
-#define PKV_LAUNCH(kernel, kSplit, kBf16) hipLaunchKernelGGL((kernel<kSplit, kBf16, kFused>), grid, block, 0, stream, p)
+#define PKV_LAUNCH(kernel, kSplit, kBf16)                                                                   \
+  hipLaunchKernelGGL((kernel<kSplit, kBf16, kFused>), grid, block, 0, stream, p.block_tables,                \
+                     kFused ? p.positions : p.context_lens, p.q, p.k_new, p.v_new, p.max_blocks, p.num_kv_heads, \
+                     p.batch, p.part_pages, p)
   if (p.matrix_cores) {
     if (split) {
       if (out_bf16) PKV_LAUNCH(paged_decode_mfma_kernel, true, true);

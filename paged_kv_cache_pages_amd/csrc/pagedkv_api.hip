@@ -35,6 +35,7 @@ pkv_status copy_to_host(std::vector<int32_t> &dst, const int32_t *src, size_t n,
 }
 
 constexpr int kMaxDevices = 64;
+constexpr int32_t kMaxGridDim = 65535;  // decode grids are (KV head, sequence, partition)
 std::atomic<int32_t> g_cu_count[kMaxDevices];
 
 }  // namespace
@@ -269,6 +270,7 @@ pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, 
   if (head_dim != pkv::kHeadDim || block_size != pkv::kBlock || num_q_heads != pkv::kGroup * num_kv_heads)
     return PKV_ERR_UNSUPPORTED;
   if (batch == 0) return PKV_OK;
+  if (batch > kMaxGridDim) return PKV_ERR_SHAPE;  // one grid dimension per sequence
   if (!q || !k_pool || !v_pool || !block_tables || !out) return PKV_ERR_NULL;
   if (fused ? (!k_new || !v_new) : !context_lens) return PKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PKV_ERR_ALIGNMENT;
@@ -284,6 +286,7 @@ pkv_status decode_common(const void *q, const void *k_pool, const void *v_pool, 
   }
   part_pages = resolved_partition_pages(part_pages, max_blocks_per_seq);
   const int32_t num_parts = (max_blocks_per_seq + part_pages - 1) / part_pages;
+  if (num_parts > kMaxGridDim) return PKV_ERR_SHAPE;
   if (num_parts > 1) {
     const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, max_blocks_per_seq, part_pages);
     if (static_scratch) {

@@ -130,6 +130,7 @@ def test_decode_host_checks(lib):
     assert _decode(lib, bs=32) == UNSUP
     assert _decode(lib, hq=16) == UNSUP  # group of 2
     assert _decode(lib, batch=0) == OK
+    assert _decode(lib, batch=65536) == SHAPE  # one grid dimension per sequence
     assert _decode(lib, q=None) == NULL
     assert _decode(lib, lens=None) == NULL
     assert _decode(lib, out=FAKE + 4) == ALIGN
