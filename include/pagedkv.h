@@ -298,10 +298,15 @@ pkv_status pkv_validate_decode_host(const int32_t *block_tables, int32_t max_blo
  * through its block table (KV head h / 4, scale, FP32 online softmax), written to out (device,
  * FP32 or BF16 [num_tokens][num_q_heads][64]).  Both products run on the matrix cores with FP32
  * accumulation: q.k on the BF16 inputs (exact products); p.v with V converted to FP16 (exact for
- * every BF16 value up to 65280) and each weight rounded to FP16 (11 significant bits, nearest
- * even), the denominator summing the same rounded weights.  A query tile whose keys hold a finite
- * V magnitude above 65504 is recomputed with BF16 V and each weight as two BF16 terms (about 16
- * significant bits, not exact).  The prompt's own rows must already be in the pool (call the
+ * every BF16 value up to 65280) and each weight, scaled by 2^7 (it cancels in the ratio), rounded
+ * to FP16 (11 significant bits, nearest even), the denominator summing the same rounded weights.
+ * The weight of a key stays a normal FP16 number down to 2^-21 of the row's anchor weight; below
+ * that it keeps an absolute error of at most 2^-25 (times 2^-7 after the scale cancels), so an
+ * output row's error is about 2^-11 of the weighted |V| plus, at worst, n * 2^-32 * max|V| over n
+ * keys.  Precision limit: with |V| of order 1e3 on rows of thousands of keys whose output dims
+ * cancel to near 0, that can exceed an absolute error of 2e-3 (still below the BF16 output's own
+ * rounding).  A query tile whose keys hold a finite V magnitude above 65504 is recomputed with
+ * BF16 V and each weight as two BF16 terms (about 16 significant bits, not exact).  The prompt's own rows must already be in the pool (call the
  * append first, on the same stream).  When start < 0, start + length > 16 * max_blocks_per_seq or
  * any of the sequence's first ceil((start + length) / 16) entries is outside [0, num_pages), all
  * its rows get zeros.  Slots past the last prompt position are never read.

@@ -23,7 +23,8 @@
 // Q and K enter the first product as the BF16 inputs they are (exact).  For the second product V
 // is staged as FP16, which holds every BF16 value up to 65280 exactly (smaller than 2^-14 in
 // magnitude only to within 2^-25), and the probabilities enter as FP16 (11 significant bits,
-// round to nearest even), so the second product needs one FP16 MFMA per tile.  A tile whose V
+// round to nearest even, scaled by 2^7 so that they leave FP16's subnormal range only below 2^-21
+// of the anchor's weight), so the second product needs one FP16 MFMA per tile.  A tile whose V
 // holds a larger finite magnitude is computed again in a second pass with BF16 V and each
 // probability carried as two BF16 terms (hi + lo, about 16 significant bits; not exact).  The
 // prompt's own K/V rows must be finite: a causally masked key still enters the second product
@@ -261,13 +262,19 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
     if (!kWide && amax > kF16Max) s_wide[buf] = c;
   };
 
-  // Per column block: output tile, softmax anchor (log2 units, shared by the 4 lanes of a query;
-  // it moves only when a weight exceeds 2^8, so most steps leave the accumulators alone) and the
-  // denominator (an MFMA accumulator, the same in all 4 rows).
+  // Per column block: output tile, softmax anchor (log2 units, shared by the 4 lanes of a query,
+  // less the pass's weight shift; it moves only when a score exceeds it by more than 8 plus that
+  // shift, so most steps leave the accumulators alone) and the denominator (an MFMA accumulator,
+  // the same in all 4 rows).
   f32x4 o[kSub][4];
   f32x4 lsum[kSub];
   float m[kSub];
-  constexpr float kHeadroomScale = 256.0f;  // 2^8
+  // Every weight carries an extra factor 2^7 (numerator and denominator alike, so the output is
+  // unchanged): in FP16, weights down to 2^-21 of the anchor's stay normal numbers (unscaled,
+  // everything below 2^-14 would be subnormal and below 2^-25 zero), and with the anchor's 2^8
+  // headroom the largest weight is 2^15, inside FP16's range.
+  constexpr float kShift = 7.0f;                     // log2 of the weight factor
+  constexpr float kHeadroomScale = 256.0f * 128.0f;  // 2^8 times the factor
   const u32x4 kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};     // BF16 1.0 x 8
   const u32x4 kOnesF16 = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // FP16 1.0 x 8
   const float c_log2 = p.score_log2;
@@ -340,7 +347,8 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
       }
 
       // Weights with the current anchor.  The anchor moves only when a weight of the step exceeds
-      // 2^8 (or is infinite: always so on the first step, where m = -inf); that test runs on the
+      // 2^8 times the pass's weight factor (or is infinite: always so on the first step, where
+      // m = -inf); that test runs on the
       // exp2 results, which need no NaN canonicalisation before v_max3, and the exact row maximum
       // is taken only on the rare step that moves the anchor.
       float pe[kSub][kHalves][8];
@@ -380,7 +388,10 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
                                    fmaxf(s[sub][hs][t][2], s[sub][hs][t][3])));
           mx = wave_xor_max(mx, 16);
           mx = wave_xor_max(mx, 32);
-          mx *= c_log2;  // scale > 0; finite: key 0 is visible to every query in step 0
+          // scale > 0; finite: key 0 is visible to every query in step 0.  The shift goes in as
+          // -4 - 2 - 1, inline constants: a 7.0 literal would take a register the loop lacks.
+          static_assert(kShift == 4.0f + 2.0f + 1.0f, "weight shift");
+          mx = __builtin_fmaf(mx, c_log2, -4.0f) - 2.0f - 1.0f;
           const float m_new = fmaxf(m[sub], mx);
           const float alpha = __builtin_amdgcn_exp2f(m[sub] - m_new);
           m[sub] = m_new;

@@ -194,6 +194,35 @@ def test_prefill_values_past_fp16_range(gpu, out_dtype):
     assert np.abs(ref).max() > 1e20  # the planted prefix value reaches the outputs
 
 
+def test_prefill_small_weights_behind_a_dominant_first_key(gpu):
+    """Rows whose first key dominates by 25.2 in log2 units (q = 16 e_0; that key's K = 8.75 e_0,
+    every other K = 0), with V = 0 there and V = 1000 on the other 4095 keys. The anchor is set
+    on the first step, so every later weight is 2^-25.2 of it: under FP16's smallest subnormal.
+    FP16 weights without the kernel's fixed 2^7 factor would drop them all (output 0 instead of
+    about 0.1); with it they are 2^-18.2, subnormal but kept. Every row must match the oracle."""
+    import torch
+
+    w = make_prefill(41, [16], [4080], max_blocks=256)
+    k_pool = np.zeros_like(w.k_pool)
+    v_pool = np.full_like(w.v_pool, f32_to_bf16_bits(np.array([1000.0], dtype=np.float32))[0])
+    first = int(w.block_tables[0, 0])
+    k_pool[first, :, 0, 0] = f32_to_bf16_bits(np.array([8.75], dtype=np.float32))[0]
+    v_pool[first, :, 0, :] = 0
+    q = np.zeros_like(w.q)
+    q[:, :, 0] = f32_to_bf16_bits(np.array([16.0], dtype=np.float32))[0]
+    w.k_pool, w.v_pool, w.q = k_pool, v_pool, q
+    w.k_new = np.zeros_like(w.k_new)
+    w.v_new = np.full_like(w.v_new, f32_to_bf16_bits(np.array([1000.0], dtype=np.float32))[0])
+    print("[prefill] small weights behind a dominant first key, 16 rows behind 4080 cached", flush=True)
+    d = upload(w)
+    out = run(gpu, d, torch.float32).cpu().numpy()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new,
+                                      w.v_new)
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos)
+    assert ref.min() > 0.09  # what the small weights carry
+    assert_close(out, ref, "small weights behind a dominant key")
+
+
 @pytest.mark.parametrize("shape", ["32 rows, 32-key steps", "32 rows, 64-key steps"])
 def test_prefill_values_past_fp16_range_every_launch_shape(gpu, shape):
     """The same second pass in the two 32-row launch shapes (the 16-row one is covered above):
