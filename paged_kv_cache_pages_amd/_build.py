@@ -23,6 +23,9 @@ LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
 # a GPU test, never part of the library.
 CLIENT_SRC = os.path.join(ROOT, "tests", "host", "abi_client.cpp")
 CLIENT_PATH = os.path.join(ROOT, "tests", "host", "pkv_abi_client")
+# A stand-alone read-bandwidth probe for the decode kernels' access pattern (measurement only).
+CEILING_SRC = os.path.join(ROOT, "tests", "host", "read_ceiling.hip")
+CEILING_PATH = os.path.join(ROOT, "tests", "host", "pkv_read_ceiling")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_SOURCES = ["pagedkv_api.hip", "kv_append.hip", "paged_attention.hip", "rope_append.hip", "prefill.hip"]
@@ -95,6 +98,10 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
               "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../paged_kv_cache_pages_amd/lib",
               "-Wl,-rpath," + os.path.join(ROCM, "lib")], verbose)
         os.replace(client_tmp, CLIENT_PATH)
+    if os.path.exists(CEILING_SRC):
+        ceiling_tmp = CEILING_PATH + ".tmp"
+        _run([hipcc, *HIP_FLAGS, CEILING_SRC, "-o", ceiling_tmp], verbose)
+        os.replace(ceiling_tmp, CEILING_PATH)
     return LIB_PATH
 
 
