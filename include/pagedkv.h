@@ -242,8 +242,8 @@ int32_t pkv_plan_partition_pages(int32_t batch, int32_t num_kv_heads, int32_t ma
 /*
  * The same plan for a batch whose longest context (tokens attended, the new one included) is
  * max_context_len, a bound the caller's scheduler knows on the host: L is then that context's
- * pages instead of the table width, so short batches run unsplit (no merge kernel) and long ones
- * split by their real length.  max_context_len < 0 means unknown (the plain plan); -1 on bad
+ * pages instead of the table width, so short batches run unsplit (no partials to publish and
+ * merge) and long ones split by their real length.  max_context_len < 0 means unknown (the plain plan); -1 on bad
  * arguments.  Only the launch shape depends on it: a context longer than the bound is still
  * attended correctly, through partitions of the returned size.
  */
