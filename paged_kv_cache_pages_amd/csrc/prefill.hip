@@ -130,17 +130,23 @@ __device__ __forceinline__ void store_row4(void *out, int64_t elem, f32x4 v) {
 // light ones fill the tail.  (Grouping a sequence's tiles on one XCD for L2 reuse was slower: it
 // gives up that order and unbalances the XCDs when prompts differ in length.)
 constexpr int kLdsPages = 256;  // block-table entries kept in LDS (4096 tokens); the rest from HBM
+// Tables up to this width are copied to LDS whole (2 KiB; every launch shape still fits its
+// workgroups per CU) and every page id is an LDS read.  With wider tables the ids past kLdsPages
+// come from the table in memory, and the choice between the two becomes one flat load per step,
+// whose completion every LDS wait of the step also waits for.
+constexpr int kLdsTableMax = 512;
 constexpr float kF16Max = 65504.0f;  // largest finite FP16 value
 
 // kChunk keys per step: 64 (two 32-key halves; 165 VGPRs with kSub = 2, 3 waves per SIMD) or 32
 // (one half; fits 128 VGPRs, so 4 waves per SIMD, at twice the steps and barriers per key).
-template <int kSub, int kChunk, bool kOutBf16>
+template <int kSub, int kChunk, bool kOutBf16, bool kTableLds>
 __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, int32_t tiles) {
   constexpr int kHalves = kChunk / 32;  // 32-key halves per step
   constexpr int kVecs = kChunk / 32;    // 16-byte K (and V) vectors each thread stages per step
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kChunk * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kChunk * kKStride];  // FP16 (BF16 in a second pass)
-  __shared__ int32_t s_pages[kLdsPages];
+  constexpr int kPageSlots = kTableLds ? kLdsTableMax : kLdsPages;
+  __shared__ int32_t s_pages[kPageSlots];
   __shared__ int32_t s_bad[kThreads / 64];
   __shared__ int32_t s_wide[2];  // step index whose staged V holds a value past FP16's range
   constexpr int kRows = 16 * kSub;  // query rows per workgroup
@@ -192,7 +198,7 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
     for (int e = tid; e < need; e += kThreads) {
       const int32_t pg = table[e];
       bad |= pg < 0 || pg >= p.num_pages;
-      if (e < kLdsPages) s_pages[e] = pg;
+      if (e < kPageSlots) s_pages[e] = pg;
     }
   }
   // Workgroup OR of `bad`: one flag per wavefront in LDS and one barrier, which also publishes
@@ -228,7 +234,8 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   auto page_of = [&](int c) -> int32_t {
     const int kp = c * kChunk + st_key;
     const int e = kp < n_keys ? kp / kBlock : 0;
-    return e < kLdsPages ? s_pages[e] : table[e];
+    if constexpr (kTableLds) return s_pages[e];  // e < need <= max_blocks <= kLdsTableMax
+    else return e < kLdsPages ? s_pages[e] : table[e];
   };
   struct Rows {
     u32x4 k[kVecs], v[kVecs];
@@ -494,15 +501,15 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
 }
 
 
-template <int kSub, bool kOutBf16>
+template <int kSub, bool kOutBf16, bool kTableLds>
 __global__ __launch_bounds__(kThreads) void prefill_attention_kernel(PrefillParams p, int32_t tiles) {
-  prefill_attention_body<kSub, 64, kOutBf16>(p, tiles);
+  prefill_attention_body<kSub, 64, kOutBf16, kTableLds>(p, tiles);
 }
 
-template <int kSub, bool kOutBf16>
+template <int kSub, bool kOutBf16, bool kTableLds>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void prefill_attention_kernel_k32(
     PrefillParams p, int32_t tiles) {
-  prefill_attention_body<kSub, 32, kOutBf16>(p, tiles);
+  prefill_attention_body<kSub, 32, kOutBf16, kTableLds>(p, tiles);
 }
 
 }  // namespace
@@ -516,21 +523,27 @@ hipError_t launch_prefill_append(const PrefillParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int kSub, bool kK32>
-hipError_t launch_attention(const PrefillParams &p, bool out_bf16, hipStream_t stream) {
+template <int kSub, bool kK32, bool kTableLds>
+hipError_t launch_attention_table(const PrefillParams &p, bool out_bf16, hipStream_t stream) {
   const int64_t tiles = ((int64_t)p.max_prompt_len + 16 * kSub - 1) / (16 * kSub);
   const int64_t blocks = tiles * p.batch * p.num_kv_heads;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(kThreads);
   if constexpr (kK32) {
-    if (out_bf16) hipLaunchKernelGGL((prefill_attention_kernel_k32<kSub, true>), grid, block, 0, stream, p, (int32_t)tiles);
-    else hipLaunchKernelGGL((prefill_attention_kernel_k32<kSub, false>), grid, block, 0, stream, p, (int32_t)tiles);
+    if (out_bf16) hipLaunchKernelGGL((prefill_attention_kernel_k32<kSub, true, kTableLds>), grid, block, 0, stream, p, (int32_t)tiles);
+    else hipLaunchKernelGGL((prefill_attention_kernel_k32<kSub, false, kTableLds>), grid, block, 0, stream, p, (int32_t)tiles);
   } else {
-    if (out_bf16) hipLaunchKernelGGL((prefill_attention_kernel<kSub, true>), grid, block, 0, stream, p, (int32_t)tiles);
-    else hipLaunchKernelGGL((prefill_attention_kernel<kSub, false>), grid, block, 0, stream, p, (int32_t)tiles);
+    if (out_bf16) hipLaunchKernelGGL((prefill_attention_kernel<kSub, true, kTableLds>), grid, block, 0, stream, p, (int32_t)tiles);
+    else hipLaunchKernelGGL((prefill_attention_kernel<kSub, false, kTableLds>), grid, block, 0, stream, p, (int32_t)tiles);
   }
   return hipGetLastError();
+}
+
+template <int kSub, bool kK32>
+hipError_t launch_attention(const PrefillParams &p, bool out_bf16, hipStream_t stream) {
+  if (p.max_blocks <= kLdsTableMax) return launch_attention_table<kSub, kK32, true>(p, out_bf16, stream);
+  return launch_attention_table<kSub, kK32, false>(p, out_bf16, stream);
 }
 
 // Two 16-query blocks per wavefront halve the LDS traffic, staging and barriers per score (16

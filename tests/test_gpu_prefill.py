@@ -123,15 +123,16 @@ def test_prefill_rows_equal_decode_kernel(gpu):
     assert np.all(np.abs(a - b) <= 4e-3 + 2e-2 * np.abs(b))
 
 
-def test_prefill_behind_prefixes_longer_than_the_staged_table(gpu):
-    """The kernel keeps the first 256 table entries (4096 tokens) in LDS and reads the rest from
-    HBM: prompt chunks behind cached prefixes of 4050 to 4200 tokens in a 300-page table read
-    both, and match the oracle."""
+@pytest.mark.parametrize("width", [300, 600])
+def test_prefill_behind_prefixes_longer_than_the_staged_table(gpu, width):
+    """Prompt chunks behind cached prefixes of 4050 to 4200 tokens (past 256 table entries) match
+    the oracle in both table forms: a 300-entry table is copied to LDS whole; with a 600-entry
+    table the kernel keeps the first 256 entries in LDS and reads the rest from HBM."""
     import torch
 
     lens, starts = [48, 30, 5], [4200, 4050, 4090]
-    w = make_prefill(27, lens, starts, max_blocks=300)
-    print(f"[prefill] long prefixes lens={lens} starts={starts}", flush=True)
+    w = make_prefill(27, lens, starts, max_blocks=width)
+    print(f"[prefill] long prefixes lens={lens} starts={starts} table width={width}", flush=True)
     d = upload(w)
     out = run(gpu, d, torch.float32)
     torch.cuda.synchronize()
