@@ -374,6 +374,19 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(PKV_PRELOADED_AR
   const bool len_ok = L >= 0 && L <= p.max_blocks * kBlock;
   const int n_pages = len_ok ? (L + kBlock - 1) / kBlock : 0;
   const int p1 = min(p0 + p.part_pages, n_pages);
+  // The parameter-struct fields used past the prologue are requested now too, so their scalar
+  // loads share the prologue's round trip instead of taking one of their own after it.
+  const int num_pages = p.num_pages;
+  const float c_log2 = p.score_log2;
+  const uint16_t *const k_pool = p.k_pool;
+  const uint16_t *const v_pool = p.v_pool;
+  asm volatile("" ::"s"(num_pages), "s"(c_log2), "s"(k_pool), "s"(v_pool));
+  if (kSplit) {
+    asm volatile("" ::"s"(p.out), "s"(p.part_o), "s"(p.part_ml), "s"(p.counters), "s"(p.num_parts));
+  } else {
+    asm volatile("" ::"s"(p.out));
+  }
+  if (kFused) asm volatile("" ::"s"(p.k_pool_w), "s"(p.v_pool_w));
   // Keep those reads above the branch below (the compiler would otherwise sink them past it,
   // behind the length read).
   asm volatile("" ::"v"(ids_row));
@@ -391,21 +404,19 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(PKV_PRELOADED_AR
     return;
   }
 
-  const float c_log2 = p.score_log2;
-
   // Pages of this wavefront: local index k -> logical page p0 + wave + kWaves * k, k < n_w <= 64
   // (a partition holds at most kMaxPartitionPages pages).
   int n_w = (p1 - p0 - wave + kWaves - 1) / kWaves;
   if (n_w < 0) n_w = 0;
   // One table entry per lane, range-checked before any page is touched.
   const int ids = lane < n_w ? ids_row : 0;
-  const bool bad = __builtin_amdgcn_ballot_w64(ids < 0 || ids >= p.num_pages) != 0;
+  const bool bad = __builtin_amdgcn_ballot_w64(ids < 0 || ids >= num_pages) != 0;
   // The wavefront holding the sequence's last page (it always holds the new token).
   const bool holds_last = n_w > 0 && p1 == n_pages && p0 + wave + kWaves * (n_w - 1) == n_pages - 1;
   // Like pkv_kv_append, the fused append depends only on its own page entry: an invalid entry
   // elsewhere in the sequence zeroes the output but does not stop the append.
   const int last_id = holds_last ? __builtin_amdgcn_readlane(ids, n_w - 1) : -1;
-  const bool do_append = kFused && last_id >= 0 && last_id < p.num_pages;
+  const bool do_append = kFused && last_id >= 0 && last_id < num_pages;
   if (bad) n_w = 0;
   const bool owns_last = n_w > 0 && holds_last;
   // q and the table entries must have landed before the first page load is issued (the page
@@ -425,8 +436,8 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(PKV_PRELOADED_AR
 
   const int64_t head_elems = (int64_t)kBlock * kHeadDim;
   const int64_t page_elems = (int64_t)p.num_kv_heads * head_elems;
-  const uint16_t *kbase = p.k_pool + g * head_elems + lane * 8;
-  const uint16_t *vbase = p.v_pool + g * head_elems + lane * 8;
+  const uint16_t *kbase = k_pool + g * head_elems + lane * 8;
+  const uint16_t *vbase = v_pool + g * head_elems + lane * 8;
   auto page_off = [&](int k) -> int64_t { return (int64_t)__builtin_amdgcn_readlane(ids, k) * page_elems; };
 
   // The sequence's last page can be partial (L % 16 != 0) and, in the fused step, receives the
@@ -645,6 +656,20 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(PKV_PRELOAD
   const bool len_ok = L >= 0 && L <= p.max_blocks * kBlock;
   const int n_pages = len_ok ? (L + kBlock - 1) / kBlock : 0;
   const int p1 = min(p0 + p.part_pages, n_pages);
+  // The parameter-struct fields used past the prologue: their scalar loads are requested here and
+  // consumed with the prologue's vector loads below, so they arrive in the same round trip rather
+  // than in one of their own after it (the compiler would otherwise issue them after the branch).
+  const int num_pages = p.num_pages;
+  const float c_log2 = p.score_log2;
+  const uint16_t *const k_pool = p.k_pool;
+  const uint16_t *const v_pool = p.v_pool;
+  asm volatile("" ::"s"(num_pages), "s"(c_log2), "s"(k_pool), "s"(v_pool));
+  if (kSplit) {
+    asm volatile("" ::"s"(p.out), "s"(p.part_o), "s"(p.part_ml), "s"(p.counters), "s"(p.num_parts));
+  } else {
+    asm volatile("" ::"s"(p.out));
+  }
+  if (kFused) asm volatile("" ::"s"(p.k_pool_w), "s"(p.v_pool_w));
   asm volatile("" ::"v"(ids_row));
   asm volatile("" ::"v"(qf[0].x), "v"(qf[0].y), "v"(qf[0].z), "v"(qf[0].w), "v"(qf[1].x), "v"(qf[1].y), "v"(qf[1].z), "v"(qf[1].w));
   if (kFused) {
@@ -660,25 +685,21 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(PKV_PRELOAD
     return;
   }
 
-  const float c_log2 = p.score_log2;
-  // Its scalar load shares a wait counter with LDS operations: land it here, in the prologue's
-  // wait, not inside the first step (where waiting for it would also wait for the V^T reads).
-  asm volatile("" ::"s"(c_log2));
   int n_w = (p1 - p0 - wave + kWaves - 1) / kWaves;
   if (n_w < 0) n_w = 0;
   const int ids = lane < n_w ? ids_row : 0;
-  const bool bad = __builtin_amdgcn_ballot_w64(ids < 0 || ids >= p.num_pages) != 0;
+  const bool bad = __builtin_amdgcn_ballot_w64(ids < 0 || ids >= num_pages) != 0;
   const bool holds_last = n_w > 0 && p1 == n_pages && p0 + wave + kWaves * (n_w - 1) == n_pages - 1;
   const int last_id = holds_last ? __builtin_amdgcn_readlane(ids, n_w - 1) : -1;
-  const bool do_append = kFused && last_id >= 0 && last_id < p.num_pages;
+  const bool do_append = kFused && last_id >= 0 && last_id < num_pages;
   if (bad) n_w = 0;
   const bool owns_last = n_w > 0 && holds_last;
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   const int64_t head_elems = (int64_t)kBlock * kHeadDim;
   const int64_t page_elems = (int64_t)p.num_kv_heads * head_elems;
-  const uint16_t *kbase = p.k_pool + g * head_elems;
-  const uint16_t *vbase = p.v_pool + g * head_elems + lane * 8;
+  const uint16_t *kbase = k_pool + g * head_elems;
+  const uint16_t *vbase = v_pool + g * head_elems + lane * 8;
   const int tail_valid = L - (n_pages - 1) * kBlock;
   if (do_append) {
     const int slot = tail_valid - 1;
