@@ -91,15 +91,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
 // Eight BF16 values to FP16 (exact for every finite BF16 value up to 65280; the next one, 65536,
-// becomes infinity), and the largest magnitude seen so far, so the caller can tell whether all
-// of them fit.
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, float &amax) {
+// becomes infinity), and the largest magnitude seen so far as BF16 bit patterns (sign cleared;
+// two per word, compared as unsigned 16-bit integers, which orders non-negative BF16 values like
+// their magnitudes), so the caller can tell whether all of them fit: a pattern above 0x477F
+// (65280) does not.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, u16x2 &mag) {
   u32x4 y;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float lo = __builtin_bit_cast(float, x[i] << 16);
     const float hi = __builtin_bit_cast(float, x[i] & 0xFFFF0000u);
-    amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(lo), __builtin_fabsf(hi)));
+    mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, x[i] & 0x7FFF7FFFu));
     f2 v;
     v[0] = lo;
     v[1] = hi;
@@ -135,7 +138,7 @@ constexpr int kLdsPages = 256;  // block-table entries kept in LDS (4096 tokens)
 // come from the table in memory, and the choice between the two becomes one flat load per step,
 // whose completion every LDS wait of the step also waits for.
 constexpr int kLdsTableMax = 512;
-constexpr float kF16Max = 65504.0f;  // largest finite FP16 value
+constexpr uint32_t kF16MaxBf16Bits = 0x477Fu;  // 65280: the largest BF16 magnitude FP16 holds
 
 // kChunk keys per step: 64 (two 32-key halves; 165 VGPRs with kSub = 2, 3 waves per SIMD) or 32
 // (one half; fits 128 VGPRs, so 4 waves per SIMD, at twice the steps and barriers per key).
@@ -233,7 +236,7 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   // staged and its score is masked.
   auto page_of = [&](int c) -> int32_t {
     const int kp = c * kChunk + st_key;
-    const int e = kp < n_keys ? kp / kBlock : 0;
+    const int e = kp < n_keys ? kp >> 4 : 0;
     if constexpr (kTableLds) return s_pages[e];  // e < need <= max_blocks <= kLdsTableMax
     else return e < kLdsPages ? s_pages[e] : table[e];
   };
@@ -242,7 +245,7 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   };
   auto load_step = [&](int c, int32_t pg, Rows &x) {
     const int kp = c * kChunk + st_key;
-    const int64_t off = (((int64_t)pg * p.num_kv_heads + g) * kBlock + kp % kBlock) * kHeadDim + st_dim;
+    const int64_t off = (((int64_t)pg * p.num_kv_heads + g) * kBlock + (kp & 15)) * kHeadDim + st_dim;
 #pragma unroll
     for (int e = 0; e < kVecs; ++e) {
       x.k[e] = *reinterpret_cast<const u32x4 *>(p.k_pool + off + 32 * e);
@@ -259,14 +262,14 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
 #pragma unroll
         for (int e = 0; e < kVecs; ++e) x.v[e] = u32x4{0, 0, 0, 0};
     }
-    float amax = 0.0f;
+    u16x2 mag = {0, 0};
 #pragma unroll
     for (int e = 0; e < kVecs; ++e) {
       *reinterpret_cast<u32x4 *>(&s_k[buf][st_key * kKStride + st_dim + 32 * e]) = x.k[e];
       *reinterpret_cast<u32x4 *>(&s_v[buf][st_key * kKStride + st_dim + 32 * e]) =
-          kWide ? x.v[e] : bf16x8_to_f16x8(x.v[e], amax);
+          kWide ? x.v[e] : bf16x8_to_f16x8(x.v[e], mag);
     }
-    if (!kWide && amax > kF16Max) s_wide[buf] = c;
+    if (!kWide && (mag.x > kF16MaxBf16Bits || mag.y > kF16MaxBf16Bits)) s_wide[buf] = c;
   };
 
   // Per column block: output tile, softmax anchor (log2 units, shared by the 4 lanes of a query,
