@@ -139,6 +139,7 @@ constexpr int kLdsPages = 256;  // block-table entries kept in LDS (4096 tokens)
 // whose completion every LDS wait of the step also waits for.
 constexpr int kLdsTableMax = 512;
 constexpr uint32_t kF16MaxBf16Bits = 0x477Fu;  // 65280: the largest BF16 magnitude FP16 holds
+constexpr uint32_t kF16FiniteMaxBits = 0x7BFFu;  // 65504: the largest finite FP16 value
 
 // kChunk keys per step: 64 (two 32-key halves; 165 VGPRs with kSub = 2, 3 waves per SIMD) or 32
 // (one half; fits 128 VGPRs, so 4 waves per SIMD, at twice the steps and barriers per key).
@@ -273,18 +274,20 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   };
 
   // Per column block: output tile, softmax anchor (log2 units, shared by the 4 lanes of a query,
-  // less the pass's weight shift; it moves only when a score exceeds it by more than 8 plus that
-  // shift, so most steps leave the accumulators alone) and the denominator (an MFMA accumulator,
+  // less the weight shift; it moves only when a weight outgrows the pass's headroom, so most
+  // steps leave the accumulators alone) and the denominator (an MFMA accumulator,
   // the same in all 4 rows).
   f32x4 o[kSub][4];
   f32x4 lsum[kSub];
   float m[kSub];
   // Every weight carries an extra factor 2^7 (numerator and denominator alike, so the output is
   // unchanged): in FP16, weights down to 2^-21 of the anchor's stay normal numbers (unscaled,
-  // everything below 2^-14 would be subnormal and below 2^-25 zero), and with the anchor's 2^8
-  // headroom the largest weight is 2^15, inside FP16's range.
+  // everything below 2^-14 would be subnormal and below 2^-25 zero).  The FP16 pass moves the
+  // anchor when a packed weight has overflowed to infinity, i.e. a score more than about 9 above
+  // it (the largest weight kept is 65504); the BF16 pass, whose weights have FP32's range, when a
+  // weight exceeds 2^8 times the factor.
   constexpr float kShift = 7.0f;                     // log2 of the weight factor
-  constexpr float kHeadroomScale = 256.0f * 128.0f;  // 2^8 times the factor
+  constexpr float kHeadroomScale = 256.0f * 128.0f;  // BF16 pass: 2^8 times the factor
   const u32x4 kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};     // BF16 1.0 x 8
   const u32x4 kOnesF16 = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // FP16 1.0 x 8
   const float c_log2 = p.score_log2;
@@ -356,18 +359,28 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
         }
       }
 
-      // Weights with the current anchor.  The anchor moves only when a weight of the step exceeds
-      // 2^8 times the pass's weight factor (or is infinite: always so on the first step, where
-      // m = -inf); that test runs on the
-      // exp2 results, which need no NaN canonicalisation before v_max3, and the exact row maximum
-      // is taken only on the rare step that moves the anchor.
+      // Weights with the current anchor.  The anchor moves only when a weight of the step outgrows
+      // the pass's headroom (always so on the first step, where m = -inf); the test runs on the
+      // exp2 results (FP16 pass: on their packed FP16 bits), which need no NaN canonicalisation,
+      // and the exact row maximum is taken only on the rare step that moves the anchor.
       float pe[kSub][kHalves][8];
+      u32x4 pw[kSub][kHalves];  // FP16 pass: the same weights packed to FP16 (nearest even)
       auto weights = [&](int sub) {
 #pragma unroll
-        for (int hs = 0; hs < kHalves; ++hs)
+        for (int hs = 0; hs < kHalves; ++hs) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             pe[sub][hs][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][hs][e >> 2][e & 3], c_log2, -m[sub]));
+          if constexpr (!kWide) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              f2 w2;
+              w2[0] = pe[sub][hs][2 * e];
+              w2[1] = pe[sub][hs][2 * e + 1];
+              pw[sub][hs][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, h2));
+            }
+          }
+        }
       };
       // On a tile's first step the anchor is still -inf, so the exact maximum is taken at once
       // instead of computing the weights twice.
@@ -377,13 +390,24 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
 #pragma unroll
         for (int sub = 0; sub < kSub; ++sub) {
           weights(sub);
-          float pm = 0.0f;
+          if constexpr (kWide) {
+            float pm = 0.0f;
 #pragma unroll
-          for (int hs = 0; hs < kHalves; ++hs)
+            for (int hs = 0; hs < kHalves; ++hs)
 #pragma unroll
-            for (int e = 0; e < 8; e += 2)
-              pm = __builtin_fmaxf(pm, __builtin_fmaxf(pe[sub][hs][e], pe[sub][hs][e + 1]));
-          over |= !(pm <= kHeadroomScale);
+              for (int e = 0; e < 8; e += 2)
+                pm = __builtin_fmaxf(pm, __builtin_fmaxf(pe[sub][hs][e], pe[sub][hs][e + 1]));
+            over |= !(pm <= kHeadroomScale);
+          } else {
+            // The packed weights are non-negative FP16 numbers, so their bit patterns order like
+            // their values: one that rounded to infinity (0x7C00) has outgrown the anchor.
+            u16x2 wmax = {0, 0};
+#pragma unroll
+            for (int hs = 0; hs < kHalves; ++hs)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) wmax = __builtin_elementwise_max(wmax, __builtin_bit_cast(u16x2, pw[sub][hs][e]));
+            over |= wmax.x > kF16FiniteMaxBits || wmax.y > kF16FiniteMaxBits;
+          }
         }
       }
       if (first || __builtin_amdgcn_ballot_w64(over)) {  // wave-uniform
@@ -436,15 +460,9 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
 #pragma unroll
           for (int sub = 0; sub < kSub; ++sub) {
             if constexpr (!kWide) {
-              // The weights enter the product as FP16 (11 significant bits, round to nearest even).
-              u32x4 ph;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                f2 w2;
-                w2[0] = pe[sub][hs][2 * e];
-                w2[1] = pe[sub][hs][2 * e + 1];
-                ph[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, h2));
-              }
+              // The weights enter the product as FP16 (11 significant bits, round to nearest even),
+              // packed when they were computed.
+              const u32x4 ph = pw[sub][hs];
               // One 16-dim tile at a time; the denominator rides along as an all-ones tile (every
               // row of it is the query's sum of the same FP16 weights).
 #pragma unroll
