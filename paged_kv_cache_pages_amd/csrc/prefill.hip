@@ -150,7 +150,11 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kChunk * kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kChunk * kKStride];  // FP16 (BF16 in a second pass)
   constexpr int kPageSlots = kTableLds ? kLdsTableMax : kLdsPages;
-  __shared__ int32_t s_pages[kPageSlots];
+  // Slots past the sequence's pages that a step's page-id lookup may reach (keys past the tile's
+  // last query, up to two steps ahead): they hold the sequence's first page (valid; those keys
+  // are masked), so the lookup needs no bounds test.
+  constexpr int kTail = kTableLds ? 2 * kChunk / kBlock : 0;
+  __shared__ int32_t s_pages[kPageSlots + kTail];
   __shared__ int32_t s_bad[kThreads / 64];
   __shared__ int32_t s_wide[2];  // step index whose staged V holds a value past FP16's range
   constexpr int kRows = 16 * kSub;  // query rows per workgroup
@@ -199,10 +203,14 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   int bad = !(start >= 0 && (int64_t)start + n <= (int64_t)p.max_blocks * kBlock);
   if (!bad) {
     const int need = (start + n + kBlock - 1) / kBlock;
-    for (int e = tid; e < need; e += kThreads) {
-      const int32_t pg = table[e];
-      bad |= pg < 0 || pg >= p.num_pages;
-      if (e < kPageSlots) s_pages[e] = pg;
+    for (int e = tid; e < need + kTail; e += kThreads) {
+      if (e < need) {
+        const int32_t pg = table[e];
+        bad |= pg < 0 || pg >= p.num_pages;
+        if (e < kPageSlots) s_pages[e] = pg;
+      } else {
+        s_pages[e] = table[0];  // checked by the thread that reads entry 0 (need >= 1)
+      }
     }
   }
   // Workgroup OR of `bad`: one flag per wavefront in LDS and one barrier, which also publishes
@@ -237,20 +245,32 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
   // staged and its score is masked.
   auto page_of = [&](int c) -> int32_t {
     const int kp = c * kChunk + st_key;
-    const int e = kp < n_keys ? kp >> 4 : 0;
-    if constexpr (kTableLds) return s_pages[e];  // e < need <= max_blocks <= kLdsTableMax
-    else return e < kLdsPages ? s_pages[e] : table[e];
+    if constexpr (kTableLds) {
+      // c <= n_chunks, so kp < n_keys + 2 kChunk: the index stays below need + kTail.
+      return s_pages[kp >> 4];
+    } else {
+      const int e = kp < n_keys ? kp >> 4 : 0;
+      return e < kLdsPages ? s_pages[e] : table[e];
+    }
   };
   struct Rows {
     u32x4 k[kVecs], v[kVecs];
   };
+  // This thread's row of a page (KV head g, token slot, dims) sits at the same offset inside every
+  // page (a step spans whole pages), so a step's address is one page-stride product away.
+  static_assert(kChunk % kBlock == 0, "steps cover whole pages");
+  // Page ids are validated (0 <= id < num_pages), so the offset is one unsigned 32 x 32 -> 64-bit
+  // multiply-add.
+  const uint32_t page_bytes = (uint32_t)p.num_kv_heads * kBlock * kHeadDim * sizeof(uint16_t);
+  const int64_t row_elems = ((int64_t)g * kBlock + (st_key & (kBlock - 1))) * kHeadDim + st_dim;
+  const char *const k_row = reinterpret_cast<const char *>(p.k_pool + row_elems);
+  const char *const v_row = reinterpret_cast<const char *>(p.v_pool + row_elems);
   auto load_step = [&](int c, int32_t pg, Rows &x) {
-    const int kp = c * kChunk + st_key;
-    const int64_t off = (((int64_t)pg * p.num_kv_heads + g) * kBlock + (kp & 15)) * kHeadDim + st_dim;
+    const uint64_t off = (uint64_t)(uint32_t)pg * page_bytes;
 #pragma unroll
     for (int e = 0; e < kVecs; ++e) {
-      x.k[e] = *reinterpret_cast<const u32x4 *>(p.k_pool + off + 32 * e);
-      x.v[e] = *reinterpret_cast<const u32x4 *>(p.v_pool + off + 32 * e);
+      x.k[e] = *reinterpret_cast<const u32x4 *>(k_row + off + 64 * e);
+      x.v[e] = *reinterpret_cast<const u32x4 *>(v_row + off + 64 * e);
     }
   };
   // kWide = false: V is staged as FP16, and a step whose V holds a magnitude past FP16's largest
