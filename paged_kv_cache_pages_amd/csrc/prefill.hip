@@ -447,11 +447,13 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
           static_assert(kShift == 4.0f + 2.0f + 1.0f, "weight shift");
           mx = __builtin_fmaf(mx, c_log2, -4.0f) - 2.0f - 1.0f;
           const float m_new = fmaxf(m[sub], mx);
-          const float alpha = __builtin_amdgcn_exp2f(m[sub] - m_new);
-          m[sub] = m_new;
+          if (!first) {  // on a tile's first step the sums are still zero: nothing to rescale
+            const float alpha = __builtin_amdgcn_exp2f(m[sub] - m_new);
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) o[sub][dt] *= alpha;
-          lsum[sub] *= alpha;
+            for (int dt = 0; dt < 4; ++dt) o[sub][dt] *= alpha;
+            lsum[sub] *= alpha;
+          }
+          m[sub] = m_new;
           weights(sub);
         }
       }
