@@ -762,13 +762,17 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(PKV_PRELOAD
         else x.vb[0] = vnew;
       }
     }
-    // Rows past a page's valid tokens are zeroed before staging, so stale or NaN slot contents
-    // never reach the product (their weights are 0 as well).
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    if (tok >= validA) x.va[0] = z;
-    if (tok + 8 >= validA) x.vb[0] = z;
-    if (tok >= validB) x.va[1] = z;
-    if (tok + 8 >= validB) x.vb[1] = z;
+    // Only a step holding the sequence's partial last page or a missing second page has rows to
+    // mask (wave-uniform): rows past a page's valid tokens are zeroed before staging, so stale or
+    // NaN slot contents never reach the product (their weights are 0 as well).
+    const bool partial = validA < kBlock || validB < kBlock;
+    if (partial) {
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      if (tok >= validA) x.va[0] = z;
+      if (tok + 8 >= validA) x.vb[0] = z;
+      if (tok >= validB) x.va[1] = z;
+      if (tok + 8 >= validB) x.vb[1] = z;
+    }
     *reinterpret_cast<uint4 *>(sv + tok * kVStride + chunk * 8) = x.va[0];
     *reinterpret_cast<uint4 *>(sv + (tok + 8) * kVStride + chunk * 8) = x.vb[0];
     *reinterpret_cast<uint4 *>(sv + (tok + 16) * kVStride + chunk * 8) = x.va[1];
@@ -800,6 +804,8 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(PKV_PRELOAD
       sc[t] = acc;
     }
     // This lane holds keys 8 kg + 4 t + i of head r: page kg / 2 of the step, token 8 (kg & 1) + 4 t + i.
+    // Columns r >= 4 are padding (q = 0): their weights only reach output columns nobody reads,
+    // and their anchor threshold is infinite, so they never move an anchor.
     const int valid_k = kg < 2 ? validA : validB;
     float smax = -INFINITY;
 #pragma unroll
@@ -808,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(PKV_PRELOAD
       for (int i = 0; i < 4; ++i) {
         const int token = 8 * (kg & 1) + 4 * t + i;
         const float x2 = sc[t][i] * c_log2;  // scaled first: p is exactly 1 for the anchor's key
-        sc[t][i] = (r < kGroup && token < valid_k) ? x2 : -INFINITY;
+        sc[t][i] = (partial && token >= valid_k) ? -INFINITY : x2;
         smax = fmax_plain(smax, sc[t][i]);
       }
     if (__builtin_amdgcn_ballot_w64(smax > thr) != 0) {  // wave-uniform and rare
