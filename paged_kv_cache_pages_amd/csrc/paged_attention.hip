@@ -597,12 +597,15 @@ __device__ __forceinline__ u32x4_t load16_stream_v(const uint16_t *p) {
 
 // Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four key groups of one MFMA
 // column): each permlane swap hands every lane the pair {x[l], x[l ^ 16]} (or ^ 32) as its two
-// results, a VALU exchange with no LDS round trip.
+// results, a VALU exchange with no LDS round trip.  The pair is reinterpreted as a whole: with
+// this compiler a bit cast whose operand is one element of a vector (a[1]) reads element 0.
 __device__ __forceinline__ float max_over_key_groups(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false);
-  x = fmax_plain(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  auto c = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false);
-  return fmax_plain(__builtin_bit_cast(float, c[0]), __builtin_bit_cast(float, c[1]));
+  const f2_t a = __builtin_bit_cast(
+      f2_t, __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false));
+  x = fmax_plain(a[0], a[1]);
+  const f2_t c = __builtin_bit_cast(
+      f2_t, __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false, false));
+  return fmax_plain(c[0], c[1]);
 }
 
 // One step's loads: K rows in the A-operand layout ([tile][dim half]) and V in the coalesced

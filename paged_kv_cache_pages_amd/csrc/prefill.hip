@@ -420,12 +420,17 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
             over |= !(pm <= kHeadroomScale);
           } else {
             // The packed weights are non-negative FP16 numbers, so their bit patterns order like
-            // their values: one that rounded to infinity (0x7C00) has outgrown the anchor.
+            // their values: one that rounded to infinity (0x7C00) has outgrown the anchor.  (Each
+            // word is copied out first: with this compiler a bit cast whose operand is one element
+            // of a vector reads element 0.)
             u16x2 wmax = {0, 0};
 #pragma unroll
             for (int hs = 0; hs < kHalves; ++hs)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) wmax = __builtin_elementwise_max(wmax, __builtin_bit_cast(u16x2, pw[sub][hs][e]));
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t word = pw[sub][hs][e];
+                wmax = __builtin_elementwise_max(wmax, __builtin_bit_cast(u16x2, word));
+              }
             over |= wmax.x > kF16FiniteMaxBits || wmax.y > kF16FiniteMaxBits;
           }
         }

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from gpu_helpers import assert_close, bf16_to_bits, layer_tensors, to_gpu_bf16, to_gpu_i32, upload
-from workloads import make_config, make_custom
+from workloads import f32_to_bf16_bits, make_config, make_custom
 
 pytestmark = pytest.mark.gpu
 
@@ -182,6 +182,36 @@ def test_equal_scores_give_mean_of_values(gpu):
         mean = vals.mean(axis=0)  # [Hkv][D]
         for h in range(32):
             assert np.max(np.abs(out[b, h] - mean[h // 4])) <= 1e-5
+
+
+@pytest.mark.parametrize("batch,partition_pages", [(24, 128), (24, 4), (24, 0), (48, 0)])
+@pytest.mark.parametrize("offset", [0, 8, 40])
+def test_one_key_far_above_the_rest(gpu, batch, partition_pages, offset):
+    """Sequence b's key at token offset + b (in every KV head) is 100 e_0 and every query is
+    100 e_0, so that key scores (100 * 100 / 8) log2(e) ~ 1803 in log2 units while every other key
+    scores |100 k_0 / 8| log2(e) ~ 18 |k_0| (k_0 ~ N(0, 1)): the output is that key's V row. The
+    planted keys sit at every token slot of a two-page step (offset 0 and 8: the first step, 40: the
+    second), so a running maximum that missed any slot's score would put 2^1700 into an FP32 weight.
+    batch 24 runs the matrix-core kernel (unsplit, split in 4-page partitions, the planner's
+    choice), batch 48 the VALU kernel."""
+    w = make_custom(seed=60 + offset + batch, lengths=[96] * batch)
+    hundred = f32_to_bf16_bits(np.array([100.0], dtype=np.float32))[0]
+    w.q[:] = 0
+    w.q[..., 0] = hundred
+    planted = [offset + b for b in range(batch)]
+    for b, t in enumerate(planted):
+        page, slot = int(w.block_tables[0, b, t // 16]), t % 16
+        w.k_pool[page, :, slot, :] = 0
+        w.k_pool[page, :, slot, 0] = hundred
+    print(f"[attention] one key far above the rest: B={batch} pp={partition_pages} offset={offset}", flush=True)
+    d = upload(w)
+    out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                 partition_pages=partition_pages).cpu().numpy()
+    ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens, 0.125)
+    for b, t in enumerate(planted):  # the oracle's output is the planted key's V row
+        v_row = oracle.bf16_bits_to_f64(w.v_pool[int(w.block_tables[0, b, t // 16]), :, t % 16, :])
+        assert np.allclose(ref[b], np.repeat(v_row, 4, axis=0), rtol=0, atol=1e-12)
+    assert_close(out, ref, f"one dominant key, B={batch} pp={partition_pages} offset={offset}")
 
 
 def test_page_permutation_bit_identical(gpu):

@@ -224,6 +224,46 @@ def test_prefill_small_weights_behind_a_dominant_first_key(gpu):
     assert_close(out, ref, "small weights behind a dominant key")
 
 
+@pytest.mark.parametrize("shape", ["16 rows, 64-key steps", "32 rows, 64-key steps", "32 rows, 32-key steps"])
+def test_prefill_late_key_far_above_the_anchor(gpu, shape):
+    """A key that arrives after a tile's anchor is set and outscores it by far more than FP16's
+    range allows (every query 16 e_0; the planted key 8.75 e_0 scores 25.2 in log2 units, the
+    others 2.9 k_0 with k_0 ~ N(0, 1)): its FP16 weight, 2^7 times 2^(25.2 - anchor), overflows, and
+    the kernel must see that and move the anchor. Prompt b, KV head g plants its key at token
+    64 + (8 b + g) % 64, so over the first 8 prompts the keys sit at every token slot of a 64-key
+    step and of two 32-key steps; further prompts (as many as the launch shape needs on this
+    device) repeat the pattern. Every row of every prompt must match the oracle."""
+    import torch
+
+    cus = gpu.cu_count()
+    groups_per_prompt = 5 * 8  # 160-row prompts: 5 groups of 32 rows per KV head
+    prompts = {"16 rows, 64-key steps": 8, "32 rows, 64-key steps": -(-2 * cus // groups_per_prompt),
+               "32 rows, 32-key steps": -(-4 * cus // groups_per_prompt)}[shape]
+    prompts = max(prompts, 8)
+    if launch_shape(cus, prompts, 160) != shape:
+        pytest.skip(f"{shape} is not reachable with 160-row prompts on {cus} compute units")
+    w = make_prefill(70 + prompts, [160] * prompts, [0] * prompts)
+    sixteen = f32_to_bf16_bits(np.array([16.0], dtype=np.float32))[0]
+    planted = f32_to_bf16_bits(np.array([8.75], dtype=np.float32))[0]
+    q = np.zeros_like(w.q)
+    q[:, :, 0] = sixteen
+    k_new = w.k_new.copy()
+    k_new[:, :, 1:] = 0
+    r0 = [int(x) for x in w.cu_seqlens]
+    for b in range(prompts):
+        for g in range(8):
+            t = 64 + (8 * b + g) % 64
+            k_new[r0[b] + t, g, 0] = planted
+    w.q, w.k_new = q, k_new
+    print(f"[prefill] late key far above the anchor, {prompts} prompts x 160, launch={shape}", flush=True)
+    d = upload(w)
+    out = run(gpu, d, torch.float32).cpu().numpy()
+    rk, rv = oracle.prefill_kv_append(w.k_pool, w.v_pool, w.block_tables, w.cu_seqlens, w.start_pos, w.k_new,
+                                      w.v_new)
+    ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos)
+    assert_close(out, ref, f"late dominant key, {shape}")
+
+
 @pytest.mark.parametrize("shape", ["32 rows, 32-key steps", "32 rows, 64-key steps"])
 def test_prefill_values_past_fp16_range_every_launch_shape(gpu, shape):
     """The same second pass in the two 32-row launch shapes (the 16-row one is covered above):
