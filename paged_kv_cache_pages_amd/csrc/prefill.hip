@@ -91,18 +91,16 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 
 // Eight BF16 values to FP16 (exact for every finite BF16 value up to 65280; the next one, 65536,
-// becomes infinity), and the largest magnitude seen so far as BF16 bit patterns (sign cleared;
-// two per word, compared as unsigned 16-bit integers, which orders non-negative BF16 values like
-// their magnitudes), so the caller can tell whether all of them fit: a pattern above 0x477F
-// (65280) does not.
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, u16x2 &mag) {
+// becomes infinity), and the largest magnitude seen so far, so the caller can tell whether all of
+// them fit: one above 65280 does not.  The magnitude is an IEEE maximum (v_maximum3 with absolute
+// value modifiers, one instruction per pair; a NaN propagates and fails the caller's test).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, float &mag) {
   u32x4 y;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float lo = __builtin_bit_cast(float, x[i] << 16);
     const float hi = __builtin_bit_cast(float, x[i] & 0xFFFF0000u);
-    mag = __builtin_elementwise_max(mag, __builtin_bit_cast(u16x2, x[i] & 0x7FFF7FFFu));
+    mag = __builtin_elementwise_maximum(mag, __builtin_elementwise_maximum(__builtin_fabsf(lo), __builtin_fabsf(hi)));
     f2 v;
     v[0] = lo;
     v[1] = hi;
@@ -138,8 +136,7 @@ constexpr int kLdsPages = 256;  // block-table entries kept in LDS (4096 tokens)
 // come from the table in memory, and the choice between the two becomes one flat load per step,
 // whose completion every LDS wait of the step also waits for.
 constexpr int kLdsTableMax = 512;
-constexpr uint32_t kF16MaxBf16Bits = 0x477Fu;  // 65280: the largest BF16 magnitude FP16 holds
-constexpr uint32_t kF16FiniteMaxBits = 0x7BFFu;  // 65504: the largest finite FP16 value
+constexpr float kF16MaxBf16 = 65280.0f;  // the largest BF16 magnitude FP16 holds
 
 // kChunk keys per step: 64 (two 32-key halves; 165 VGPRs with kSub = 2, 3 waves per SIMD) or 32
 // (one half; fits 128 VGPRs, so 4 waves per SIMD, at twice the steps and barriers per key).
@@ -283,31 +280,30 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
 #pragma unroll
         for (int e = 0; e < kVecs; ++e) x.v[e] = u32x4{0, 0, 0, 0};
     }
-    u16x2 mag = {0, 0};
+    float mag = 0.0f;
 #pragma unroll
     for (int e = 0; e < kVecs; ++e) {
       *reinterpret_cast<u32x4 *>(&s_k[buf][st_key * kKStride + st_dim + 32 * e]) = x.k[e];
       *reinterpret_cast<u32x4 *>(&s_v[buf][st_key * kKStride + st_dim + 32 * e]) =
           kWide ? x.v[e] : bf16x8_to_f16x8(x.v[e], mag);
     }
-    if (!kWide && (mag.x > kF16MaxBf16Bits || mag.y > kF16MaxBf16Bits)) s_wide[buf] = c;
+    if (!kWide && !(mag <= kF16MaxBf16)) s_wide[buf] = c;
   };
 
   // Per column block: output tile, softmax anchor (log2 units, shared by the 4 lanes of a query,
-  // less the weight shift; it moves only when a weight outgrows the pass's headroom, so most
-  // steps leave the accumulators alone) and the denominator (an MFMA accumulator,
-  // the same in all 4 rows).
+  // less the weight shift; it moves only when a score outgrows the headroom, so most steps leave
+  // the accumulators alone) and the denominator (an MFMA accumulator, the same in all 4 rows).
   f32x4 o[kSub][4];
   f32x4 lsum[kSub];
   float m[kSub];
   // Every weight carries an extra factor 2^7 (numerator and denominator alike, so the output is
   // unchanged): in FP16, weights down to 2^-21 of the anchor's stay normal numbers (unscaled,
-  // everything below 2^-14 would be subnormal and below 2^-25 zero).  The FP16 pass moves the
-  // anchor when a packed weight has overflowed to infinity, i.e. a score more than about 9 above
-  // it (the largest weight kept is 65504); the BF16 pass, whose weights have FP32's range, when a
-  // weight exceeds 2^8 times the factor.
-  constexpr float kShift = 7.0f;                     // log2 of the weight factor
-  constexpr float kHeadroomScale = 256.0f * 128.0f;  // BF16 pass: 2^8 times the factor
+  // everything below 2^-14 would be subnormal and below 2^-25 zero).  The anchor moves when a
+  // score lies more than 8 (log2 units) above it, so every weight is at most 2^(8 + 7) = 32768,
+  // finite in FP16 (largest 65504).  The test takes each lane's largest raw score as soon as the
+  // score products are done, off the exponentials' path.
+  constexpr float kShift = 7.0f;              // log2 of the weight factor
+  constexpr float kLimit = 8.0f + kShift;     // largest exponent of a weight
   const u32x4 kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};     // BF16 1.0 x 8
   const u32x4 kOnesF16 = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // FP16 1.0 x 8
   const float c_log2 = p.score_log2;
@@ -379,63 +375,21 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
         }
       }
 
-      // Weights with the current anchor.  The anchor moves only when a weight of the step outgrows
-      // the pass's headroom (always so on the first step, where m = -inf); the test runs on the
-      // exp2 results (FP16 pass: on their packed FP16 bits), which need no NaN canonicalisation,
-      // and the exact row maximum is taken only on the rare step that moves the anchor.
-      float pe[kSub][kHalves][8];
-      u32x4 pw[kSub][kHalves];  // FP16 pass: the same weights packed to FP16 (nearest even)
-      auto weights = [&](int sub) {
-#pragma unroll
-        for (int hs = 0; hs < kHalves; ++hs) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pe[sub][hs][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][hs][e >> 2][e & 3], c_log2, -m[sub]));
-          if constexpr (!kWide) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              f2 w2;
-              w2[0] = pe[sub][hs][2 * e];
-              w2[1] = pe[sub][hs][2 * e + 1];
-              pw[sub][hs][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, h2));
-            }
-          }
-        }
-      };
-      // On a tile's first step the anchor is still -inf, so the exact maximum is taken at once
-      // instead of computing the weights twice.
-      const bool first = c == 0;
+      // Anchor test: does a score of the block, scaled, exceed the anchor by more than the limit
+      // (always so on the tile's first step, where the anchor is -inf)?  The exact row maximum is
+      // taken only on the rare step that moves the anchor.
+      // (IEEE maximum, NaN-propagating: v_maximum3 needs no quieting of its inputs, unlike fmaxf.)
       bool over = false;
-      if (!first) {
 #pragma unroll
-        for (int sub = 0; sub < kSub; ++sub) {
-          weights(sub);
-          if constexpr (kWide) {
-            float pm = 0.0f;
+      for (int sub = 0; sub < kSub; ++sub) {
+        float smax = s[sub][0][0][0];
 #pragma unroll
-            for (int hs = 0; hs < kHalves; ++hs)
-#pragma unroll
-              for (int e = 0; e < 8; e += 2)
-                pm = __builtin_fmaxf(pm, __builtin_fmaxf(pe[sub][hs][e], pe[sub][hs][e + 1]));
-            over |= !(pm <= kHeadroomScale);
-          } else {
-            // The packed weights are non-negative FP16 numbers, so their bit patterns order like
-            // their values: one that rounded to infinity (0x7C00) has outgrown the anchor.  (Each
-            // word is copied out first: with this compiler a bit cast whose operand is one element
-            // of a vector reads element 0.)
-            u16x2 wmax = {0, 0};
-#pragma unroll
-            for (int hs = 0; hs < kHalves; ++hs)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const uint32_t word = pw[sub][hs][e];
-                wmax = __builtin_elementwise_max(wmax, __builtin_bit_cast(u16x2, word));
-              }
-            over |= wmax.x > kF16FiniteMaxBits || wmax.y > kF16FiniteMaxBits;
-          }
-        }
+        for (int e = 1; e < 8 * kHalves; ++e)
+          smax = __builtin_elementwise_maximum(smax, s[sub][e >> 3][(e >> 2) & 1][e & 3]);
+        over |= __builtin_fmaf(smax, c_log2, -m[sub]) > kLimit;  // NaN (both -inf) is false
       }
-      if (first || __builtin_amdgcn_ballot_w64(over)) {  // wave-uniform
+      if (__builtin_amdgcn_ballot_w64(over)) {  // wave-uniform
+        const bool first = c == 0;
 #pragma unroll
         for (int sub = 0; sub < kSub; ++sub) {
           float mx = -INFINITY;
@@ -459,9 +413,30 @@ __device__ __forceinline__ void prefill_attention_body(const PrefillParams &p, i
             lsum[sub] *= alpha;
           }
           m[sub] = m_new;
-          weights(sub);
         }
       }
+
+      // Weights with the current anchor: 2^(x - m), at most 2^15; the FP16 pass packs them to FP16
+      // (nearest even) as they are made.
+      float pe[kSub][kHalves][8];
+      u32x4 pw[kSub][kHalves];
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+        for (int hs = 0; hs < kHalves; ++hs) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pe[sub][hs][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][hs][e >> 2][e & 3], c_log2, -m[sub]));
+          if constexpr (!kWide) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              f2 w2;
+              w2[0] = pe[sub][hs][2 * e];
+              w2[1] = pe[sub][hs][2 * e + 1];
+              pw[sub][hs][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, h2));
+            }
+          }
+        }
 
       // O^T += V^T P^T for the step.  kWide: the weights as hi + lo BF16 pairs against BF16 V;
       // otherwise as FP16 against the FP16 staged V.
