@@ -809,8 +809,9 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(PKV_PRELOAD
     // This lane holds keys 8 kg + 4 t + i of head r: page kg / 2 of the step, token 8 (kg & 1) + 4 t + i.
     // Columns r >= 4 are padding (q = 0): their weights only reach output columns nobody reads,
     // and their anchor threshold is infinite, so they never move an anchor.
+    // The lane's largest score is an IEEE maximum (v_maximum3, three inputs per instruction and no
+    // quieting of its inputs); scores are finite or -inf, so it equals the plain maximum.
     const int valid_k = kg < 2 ? validA : validB;
-    float smax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -818,8 +819,10 @@ __global__ __launch_bounds__(kThreads) void paged_decode_mfma_kernel(PKV_PRELOAD
         const int token = 8 * (kg & 1) + 4 * t + i;
         const float x2 = sc[t][i] * c_log2;  // scaled first: p is exactly 1 for the anchor's key
         sc[t][i] = (partial && token >= valid_k) ? -INFINITY : x2;
-        smax = fmax_plain(smax, sc[t][i]);
       }
+    float smax = sc[0][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) smax = __builtin_elementwise_maximum(smax, sc[e >> 2][e & 3]);
     if (__builtin_amdgcn_ballot_w64(smax > thr) != 0) {  // wave-uniform and rare
       const float mx = max_over_key_groups(smax);
       const float m_new = fmax_plain(m, mx);
