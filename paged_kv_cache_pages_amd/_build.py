@@ -26,6 +26,8 @@ CLIENT_PATH = os.path.join(ROOT, "tests", "host", "pkv_abi_client")
 # A stand-alone read-bandwidth probe for the decode kernels' access pattern (measurement only).
 CEILING_SRC = os.path.join(ROOT, "tests", "host", "read_ceiling.hip")
 CEILING_PATH = os.path.join(ROOT, "tests", "host", "pkv_read_ceiling")
+ISSUE_SRC = os.path.join(ROOT, "tests", "host", "issue_rate.hip")
+ISSUE_PATH = os.path.join(ROOT, "tests", "host", "pkv_issue_rate")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_SOURCES = ["pagedkv_api.hip", "kv_append.hip", "paged_attention.hip", "rope_append.hip", "prefill.hip"]
@@ -102,6 +104,10 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         ceiling_tmp = CEILING_PATH + ".tmp"
         _run([hipcc, *HIP_FLAGS, CEILING_SRC, "-o", ceiling_tmp], verbose)
         os.replace(ceiling_tmp, CEILING_PATH)
+    if os.path.exists(ISSUE_SRC):
+        issue_tmp = ISSUE_PATH + ".tmp"
+        _run([hipcc, *HIP_FLAGS, ISSUE_SRC, "-o", issue_tmp], verbose)
+        os.replace(issue_tmp, ISSUE_PATH)
     return LIB_PATH
 
 
