@@ -185,16 +185,17 @@ def test_equal_scores_give_mean_of_values(gpu):
 
 
 @pytest.mark.parametrize("batch,partition_pages", [(24, 128), (24, 4), (24, 0), (48, 0)])
-@pytest.mark.parametrize("offset", [0, 8, 40])
+@pytest.mark.parametrize("offset", [0, 8, 40, 72])
 def test_one_key_far_above_the_rest(gpu, batch, partition_pages, offset):
     """Sequence b's key at token offset + b (in every KV head) is 100 e_0 and every query is
     100 e_0, so that key scores (100 * 100 / 8) log2(e) ~ 1803 in log2 units while every other key
     scores |100 k_0 / 8| log2(e) ~ 18 |k_0| (k_0 ~ N(0, 1)): the output is that key's V row. The
     planted keys sit at every token slot of a two-page step (offset 0 and 8: the first step, 40: the
-    second), so a running maximum that missed any slot's score would put 2^1700 into an FP32 weight.
-    batch 24 runs the matrix-core kernel (unsplit, split in 4-page partitions, the planner's
-    choice), batch 48 the VALU kernel."""
-    w = make_custom(seed=60 + offset + batch, lengths=[96] * batch)
+    second, 72: the third, which 4-page partitions put in the second partition, so the merge has to
+    drop the first partition's sum by 2^-1700), so a running maximum that missed any slot's score
+    would put 2^1700 into an FP32 weight. batch 24 runs the matrix-core kernel (unsplit, split in
+    4-page partitions, the planner's choice), batch 48 the VALU kernel. Contexts are 128 tokens."""
+    w = make_custom(seed=60 + offset + batch, lengths=[128] * batch)
     hundred = f32_to_bf16_bits(np.array([100.0], dtype=np.float32))[0]
     w.q[:] = 0
     w.q[..., 0] = hundred
