@@ -28,6 +28,8 @@ CEILING_SRC = os.path.join(ROOT, "tests", "host", "read_ceiling.hip")
 CEILING_PATH = os.path.join(ROOT, "tests", "host", "pkv_read_ceiling")
 ISSUE_SRC = os.path.join(ROOT, "tests", "host", "issue_rate.hip")
 ISSUE_PATH = os.path.join(ROOT, "tests", "host", "pkv_issue_rate")
+CU_READ_SRC = os.path.join(ROOT, "tests", "host", "cu_read_rate.hip")
+CU_READ_PATH = os.path.join(ROOT, "tests", "host", "pkv_cu_read_rate")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_SOURCES = ["pagedkv_api.hip", "kv_append.hip", "paged_attention.hip", "rope_append.hip", "prefill.hip"]
@@ -108,6 +110,10 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         issue_tmp = ISSUE_PATH + ".tmp"
         _run([hipcc, *HIP_FLAGS, ISSUE_SRC, "-o", issue_tmp], verbose)
         os.replace(issue_tmp, ISSUE_PATH)
+    if os.path.exists(CU_READ_SRC):
+        cu_tmp = CU_READ_PATH + ".tmp"
+        _run([hipcc, *HIP_FLAGS, CU_READ_SRC, "-o", cu_tmp], verbose)
+        os.replace(cu_tmp, CU_READ_PATH)
     return LIB_PATH
 
 
