@@ -81,3 +81,23 @@ def test_random_prefill_steps(gpu, lengths, starts, q_scale, seed):
     assert np.array_equal(bf16_to_bits(kp), rk) and np.array_equal(bf16_to_bits(vp), rv)
     ref = oracle.paged_prefill_attention(w.q, rk, rv, w.block_tables, w.cu_seqlens, w.start_pos)
     assert_close(out.cpu().numpy(), ref, f"lengths={lengths} starts={starts} q x{q_scale}")
+
+
+@pytest.mark.parametrize("q_scale", [4.0, 32.0])
+def test_vector_kernel_on_peaked_rows(gpu, q_scale):
+    """The large-batch (VALU) kernel on peaked rows: 40 sequences of random lengths (40 x 8 pairs
+    fill the chip, so the plan is unsplit and the VALU kernel runs) with q scaled by 4 or 32."""
+    import torch
+
+    rng = np.random.default_rng(int(q_scale))
+    lengths = [int(x) for x in rng.integers(1, 701, 40)]
+    w = make_custom(seed=90 + int(q_scale), lengths=lengths)
+    w.q = scale_bf16(w.q, q_scale)
+    d = upload(w)
+    gpu.kv_append(d["k_pool"], d["v_pool"], d["block_tables"], d["positions"], d["k_new"], d["v_new"])
+    out = gpu.paged_decode_attention(d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rk, rv = oracle.kv_append(w.k_pool, w.v_pool, w.block_tables[0], w.positions, w.k_new[0], w.v_new[0])
+    ref = oracle.paged_decode_attention(w.q[0], rk, rv, w.block_tables[0], w.context_lens)
+    assert_close(out.cpu().numpy(), ref, f"VALU kernel, q x{q_scale}")
