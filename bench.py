@@ -43,6 +43,8 @@ WORKLOAD_TEXT = {
     "mixed": "16 sequences, context uniform in [1,2048], 2048-page pool",
     "model16": "16 layers, 128 MiB pool (4096 pages), FIFO-admitted batch, geometric contexts (mean 256)",
     "bw256": "256 sequences x context 2048, 32768 pages (1 GiB BF16 K+V), random page order",
+    "bw256tp8": "one GPU's share of bw256 under 8-way KV-head tensor parallelism: 256 sequences x context 2048, "
+                "1 KV head (4 query heads), 32768 pages (128 MiB BF16 K+V), random page order",
 }
 
 

@@ -31,13 +31,13 @@ def fused(gpu, q, kp, vp, bt, pos, kn, vn, pp):
     return gpu.decode_step(q, kp, vp, bt, pos, kn, vn, out_dtype=torch.float32, partition_pages=pp)
 
 
-@pytest.mark.parametrize("name", ["tiny", "long", "mixed", "model16", "bw256"])
+@pytest.mark.parametrize("name", ["tiny", "long", "mixed", "model16", "bw256", "bw256tp8"])
 def test_fused_step_equals_two_calls(gpu, name):
     import torch
 
     w = make_config(name)
     # the launch configuration bench.py times: the plan from the longest context
-    pp = gpu.plan_partition_pages(w.batch, 8, w.max_blocks, max_context=int(w.context_lens.max()))
+    pp = gpu.plan_partition_pages(w.batch, w.num_kv_heads, w.max_blocks, max_context=int(w.context_lens.max()))
     print(f"[fused] config={name} B={w.batch} layers={w.layers} partition_pages={pp}", flush=True)
     kp1, vp1 = to_gpu_bf16(w.k_pool), to_gpu_bf16(w.v_pool)
     kp2, vp2 = kp1.clone(), vp1.clone()

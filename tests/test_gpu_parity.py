@@ -16,7 +16,7 @@ from workloads import f32_to_bf16_bits, make_config, make_custom
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = ["tiny", "long", "mixed", "model16", "bw256"]
+CONFIGS = ["tiny", "long", "mixed", "model16", "bw256", "bw256tp8"]
 NAN_BITS = np.uint16(0x7FC0)
 
 _cache = {}

@@ -29,7 +29,7 @@ NUM_Q_HEADS = 32
 NUM_KV_HEADS = 8
 MAX_BLOCKS = 128  # 2048-token context / 16 tokens per page
 
-CONFIG_NAMES = ("tiny", "long", "mixed", "model16", "bw256")
+CONFIG_NAMES = ("tiny", "long", "mixed", "model16", "bw256", "bw256tp8")
 
 _CHUNK = 1 << 24
 
@@ -247,12 +247,25 @@ def make_bw256(seed: int = 4) -> Workload:
     return _finish("bw256", seed, tables, np.full(batch, L, dtype=np.int32), rows, {"sum_context": batch * L})
 
 
+def make_bw256_tp8(seed: int = 6) -> Workload:
+    """One GPU's share of bw256 under 8-way tensor parallelism over KV heads: 256 sequences at
+    context 2048, 1 KV head and its 4 query heads, 32768 pages of one head (128 MiB of BF16 K+V)."""
+    rng = np.random.default_rng(seed)
+    batch, L, hkv = 256, 2048, 1
+    num_pages = batch * MAX_BLOCKS
+    perm = rng.permutation(num_pages).astype(np.int32)
+    tables = perm.reshape(1, batch, MAX_BLOCKS).copy()
+    rows = _draw_rows(rng, 1, batch, num_pages, hkv * (NUM_Q_HEADS // NUM_KV_HEADS), hkv, HEAD_DIM)
+    return _finish("bw256tp8", seed, tables, np.full(batch, L, dtype=np.int32), rows, {"sum_context": batch * L})
+
+
 _MAKERS = {
     "tiny": make_tiny,
     "long": make_long,
     "mixed": make_mixed,
     "model16": make_model16,
     "bw256": make_bw256,
+    "bw256tp8": make_bw256_tp8,
 }
 
 
