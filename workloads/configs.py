@@ -1,4 +1,4 @@
-"""The five synthetic decode-step configurations and a generic builder.
+"""The synthetic decode-step configurations and a generic builder.
 
 Every array is produced from ``numpy.random.default_rng(seed)`` (PCG64) in a fixed draw order:
 context lengths, then the physical page permutation, then the K pool, the V pool, the queries,
@@ -270,7 +270,7 @@ _MAKERS = {
 
 
 def make_config(name: str) -> Workload:
-    """Build one of the five named configurations with its own seed (tiny=0 ... bw256=4)."""
+    """Build one of the named configurations with its own seed (tiny=0 ... bw256=4, bw256tp8=6)."""
     if name not in _MAKERS:
         raise KeyError(f"unknown config {name!r}; expected one of {CONFIG_NAMES}")
     return _MAKERS[name]()
