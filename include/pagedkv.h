@@ -232,10 +232,10 @@ pkv_status pkv_decode_step_static(const pkv_pool *pool, const void *q, const int
 /*
  * Pages per partition chosen when partition_pages <= 0.  Pure function (no GPU needed).  With L
  * the pages of the longest context (here the table width): no split when the batch *
- * num_kv_heads workgroups number at least 3/4 of num_cus; otherwise the smallest multiple of 4
- * pages, at least 16, that gives about 2 workgroups per compute unit over L, and no split if that
- * is >= L; never more than 256.  Returns min(max_blocks_per_seq, 256) when no split is planned;
- * -1 on bad arguments.
+ * num_kv_heads workgroups number at least 3/4 of num_cus, or when L <= 24; otherwise the
+ * smallest multiple of 4 pages, at least 8, that gives about one workgroup per compute unit over
+ * L, and no split if that is >= L; never more than 256.  Returns min(max_blocks_per_seq, 256)
+ * when no split is planned; -1 on bad arguments.
  */
 int32_t pkv_plan_partition_pages(int32_t batch, int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t num_cus);
 

@@ -24,9 +24,9 @@
 //     plus 8; only when a page exceeds it does the wavefront recompute the anchor and rescale
 //     its accumulators (the result is independent of the anchor; fp32 holds 2^8 of headroom).
 //   * Long contexts with few (sequence, KV head) pairs are cut into partitions.  Each publishes
-//     its (max, sum, partial output) per query head to the workspace with device-coherent stores
-//     and counts itself on a per-(sequence, KV head) counter; the partition that arrives last
-//     reads the others' partials back (device-coherent loads) and writes the output, so the split
+//     its (max, sum, partial output) per query head to the workspace with device-scope atomic
+//     swaps and counts itself on a per-(sequence, KV head) counter; the partition that arrives
+//     last swaps the others' partials out (leaving zeros) and writes the output, so the split
 //     needs no second kernel.  Workgroup ids are partition-major, so every partition index is
 //     spread over all 8 XCDs.
 // Block-table entries are read straight into a VGPR (one entry per lane) and moved to scalar
@@ -235,19 +235,23 @@ __device__ __forceinline__ int context_length(const DecodeParams &p, int b) {
     (p).part_pages = pre_part_pages; \
   } while (0)
 
-// Partitions one merging workgroup reads at once (the loads of a chunk go out together).
+// Partitions one merging workgroup reads at once (the swaps of a chunk go out together).
 constexpr int kMergeChunk = 16;
 
 // Ends a workgroup once its wavefronts' states are combined: thread (h, d) holds, for query head
 // 4 g + h and dim d, the partition's anchor M (log2 units), denominator Ls and un-normalised output
 // O; any_bad is set when the partition met an invalid table entry.  Unsplit, or a sequence whose
 // pages fit one partition: out = O / Ls (zeros when any_bad).  Otherwise the partition publishes
-// (M, Ls or -1, O) with device-coherent stores, counts itself on the (sequence, KV head) counter,
-// and the partition that arrives last merges all of them with the pairwise (max, sum) rule
+// (M, Ls or -1, O) with device-scope atomic swaps, counts itself on the (sequence, KV head)
+// counter, and the partition that arrives last merges all of them with the pairwise (max, sum) rule
 // ("The prefill path: flowing the entire prompt at once", section "causalMask and online
 // softmax"): M* = max M_i, out = sum 2^(M_i - M*) O_i / sum 2^(M_i - M*) Ls_i, or zeros when a
-// partition marked itself invalid.  The merging partition resets the counter and zeroes every
-// partial it read, so the workspace is all-zero again when the launch ends.
+// partition marked itself invalid.  The merging partition reads the partials with swaps that
+// leave zeros behind and resets the counter, so the workspace is all-zero again when the launch
+// ends.  Swaps stand in for plain stores and loads because a device-scope atomic's round trip
+// (about 0.4 us on MI355X) is well under that of a device-coherent store's acknowledgement or a
+// device-coherent load (about 1 us), and on a split step the publish, count and read-back are
+// the tail of the critical path.
 template <bool kSplit, bool kOutBf16>
 __device__ __forceinline__ void finish_group(const DecodeParams &p, int b, int g, int part, int n_pages, float M,
                                              float O, float Ls, bool any_bad) {
@@ -267,14 +271,14 @@ __device__ __forceinline__ void finish_group(const DecodeParams &p, int b, int g
   }
   const int64_t slot0 = ((int64_t)b * p.num_q_heads + qh) * p.num_parts;
   const int64_t slot = slot0 + part;
-  __hip_atomic_store(p.part_o + slot * kHeadDim + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_exchange(p.part_o + slot * kHeadDim + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (d == 0) {
-    __hip_atomic_store(p.part_ml + slot * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(p.part_ml + slot * 2 + 1, any_bad ? -1.0f : Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_exchange(p.part_ml + slot * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_exchange(p.part_ml + slot * 2 + 1, any_bad ? -1.0f : Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // Count the partition only once its partials are acknowledged (device-coherent stores write
-  // through to memory, so a partition on another XCD reads them with device-coherent loads and no
-  // whole-L2 write-back or invalidation is needed).
+  // Count the partition only once its swaps are acknowledged: a partition on another XCD then
+  // finds them with its own device-scope swaps, and no whole-L2 write-back or invalidation is
+  // needed.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   uint32_t *ctr = p.counters + ((int64_t)b * p.num_kv_heads + g) * kCounterStride;
@@ -288,12 +292,21 @@ __device__ __forceinline__ void finish_group(const DecodeParams &p, int b, int g
   bool bad = false;
   for (int i0 = 0; i0 < n_parts; i0 += kMergeChunk) {
     float mv[kMergeChunk], lv[kMergeChunk], ov[kMergeChunk];
+    // Lane 2 u + j takes word j of partition i0 + u's (max, denominator) pair: the chunk's
+    // pairs are contiguous, so one swap instruction reads (and zeroes) all of them.
+    float mlw = 0.0f;
+    if (d < 2 * kMergeChunk && i0 + (d >> 1) < n_parts)
+      mlw = __hip_atomic_exchange(ml + 2 * i0 + d, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {  // clamped indexes: every load is a published slot
-      const int i = min(i0 + u, n_parts - 1);
-      mv[u] = __hip_atomic_load(ml + 2 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      lv[u] = __hip_atomic_load(ml + 2 * i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ov[u] = __hip_atomic_load(po + (int64_t)i * kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const int i = i0 + u;  // wave-uniform
+      if (i < n_parts)
+        ov[u] = __hip_atomic_exchange(po + (int64_t)i * kHeadDim, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      mv[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mlw), 2 * u));
+      lv[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mlw), 2 * u + 1));
     }
     float Mc = Mg;
 #pragma unroll
@@ -309,13 +322,6 @@ __device__ __forceinline__ void finish_group(const DecodeParams &p, int b, int g
         Og = __builtin_fmaf(e, ov[u], Og);
         Lg = __builtin_fmaf(e, lv[u], Lg);
         bad |= !(lv[u] >= 0.0f);
-        // Consumed slots go back to zero, so every call leaves the whole workspace zero-filled
-        // and a later call of any shape finds its counters at zero.
-        __hip_atomic_store(po + (int64_t)(i0 + u) * kHeadDim, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (d == 0) {
-          __hip_atomic_store(ml + 2 * (i0 + u), 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(ml + 2 * (i0 + u) + 1, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
       }
     }
     Mg = Mc;

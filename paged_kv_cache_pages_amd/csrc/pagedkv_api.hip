@@ -75,21 +75,26 @@ extern "C" int32_t pkv_device_cu_count(void) {
 
 namespace {
 // The plan for a batch whose longest context spans `longest` pages (<= the table width).
-// Measured on the fused step replayed from a HIP graph over 20 batches (1-64 sequences, uniform
-// 1024/2048-token contexts, geometric mean-256 and uniform random lengths), every size from 4 to
-// 128 pages: this rule picks the fastest size or lands within ~7% of it.  With the partitions
-// merged inside the launch, many small partitions cost more than they save (8 pages is rarely
-// best, 4 never), and from 3/4 of a workgroup per compute unit the unsplit launch is fastest.
+// Fitted to the fused step replayed from a HIP graph, 16 layers per step, over 27 batches (1-64
+// sequences: uniform 256/384/512/1024/2048-token contexts, geometric mean-256 and uniform random
+// lengths), every size from 4 to 128 pages: on average this rule lands within 2% of the fastest
+// size.  A context of up to 24 pages runs fastest unsplit (the in-launch merge costs more than the
+// shorter page loop saves); above that, about one workgroup per compute unit over the longest
+// context is best, down to 8-page partitions (two pages per wavefront); and from 3/4 of a
+// workgroup per compute unit the unsplit launch is fastest.
+constexpr int64_t kMinSplitPages = 24;
+constexpr int64_t kMinPartitionPages = 8;
 int32_t plan_pages(int64_t pairs, int32_t max_blocks_per_seq, int64_t longest, int32_t num_cus) {
   const int32_t cap = max_blocks_per_seq < pkv::kMaxPartitionPages ? max_blocks_per_seq : pkv::kMaxPartitionPages;
   if (pairs == 0) return cap;
   if (4 * pairs >= 3LL * num_cus) return cap;
-  // About 2 workgroups per compute unit over the longest context, in equal shares for the 4
-  // wavefronts, and at least 16 pages.
-  const int64_t parts = (2LL * num_cus + pairs - 1) / pairs;
+  if (longest <= kMinSplitPages) return cap;
+  // About one workgroup per compute unit over the longest context, in equal shares for the 4
+  // wavefronts, and at least 8 pages.
+  const int64_t parts = (num_cus + pairs - 1) / pairs;
   int64_t pages = (longest + parts - 1) / parts;
   pages = ((pages + 3) / 4) * 4;
-  if (pages < 16) pages = 16;
+  if (pages < kMinPartitionPages) pages = kMinPartitionPages;
   return pages >= longest || pages >= cap ? cap : (int32_t)pages;
 }
 }  // namespace

@@ -21,6 +21,9 @@ def batches(rng):
         out.append((f"uniform 2048 x{b}", [2048] * b))
     for b in (4, 8, 16, 32):
         out.append((f"uniform 1024 x{b}", [1024] * b))
+    for length in (256, 384, 512):
+        for b in (1, 4, 16):
+            out.append((f"uniform {length} x{b}", [length] * b))
     for b in (8, 17, 32, 64):
         out.append((f"geometric mean 256 x{b}", [int(min(2048, x)) for x in rng.geometric(1 / 256, b)]))
     for b in (8, 16, 32):

@@ -48,18 +48,19 @@ def test_status_strings_and_version(lib):
 def test_partition_planning():
     plan = lambda b, h, t, c: pkv.plan_partition_pages(b, h, t, num_cus=c)
     assert plan(256, 8, 128, 256) == 128  # 2048 (sequence, head) workgroups: no split
-    assert plan(1, 8, 128, 256) == 16  # one long sequence: 8 partitions of 16 pages (the minimum)
-    assert plan(8, 8, 128, 256) == 16  # about 2 workgroups per compute unit, at least 16 pages
-    assert plan(16, 8, 128, 256) == 32
-    assert plan(17, 8, 128, 256) == 32
-    assert plan(23, 8, 128, 256) == 44  # 184 workgroups: 3 partitions of 44 pages
+    assert plan(1, 8, 128, 256) == 8  # one long sequence: 16 partitions of 8 pages (the minimum)
+    assert plan(4, 8, 128, 256) == 16  # about one workgroup per compute unit
+    assert plan(8, 8, 128, 256) == 32
+    assert plan(16, 8, 128, 256) == 64 and plan(17, 8, 128, 256) == 64 and plan(23, 8, 128, 256) == 64
     assert plan(24, 8, 128, 256) == 128 and plan(32, 8, 128, 256) == 128  # from 3/4 workgroup per CU
     assert plan(40, 8, 128, 256) == 128 and plan(64, 8, 128, 256) == 128
-    assert plan(4, 8, 16, 256) == 16 and plan(4, 8, 17, 256) == 16  # a 16-page table never splits
-    assert plan(4, 8, 48, 256) == 16  # 48 pages: 3 partitions
+    assert plan(4, 8, 16, 256) == 16 and plan(4, 8, 24, 256) == 24  # up to 24 pages: never split
+    assert plan(4, 8, 25, 256) == 8  # 25 pages: 4 partitions
+    assert plan(4, 8, 48, 256) == 8  # 48 pages: 6 partitions
+    assert plan(2, 8, 48, 256) == 8 and plan(2, 8, 128, 256) == 8
     for b in range(0, 300, 7):
         p = plan(b, 8, 128, 256)
-        assert 16 <= p <= 128 and (p == 128 or p % 4 == 0)
+        assert 8 <= p <= 128 and (p == 128 or p % 4 == 0)
     assert pkv.library().pkv_plan_partition_pages(-1, 8, 128, 256) == -1
 
 
@@ -67,20 +68,21 @@ def test_partition_planning_with_a_known_longest_context():
     plan = lambda b, t, mc: pkv.plan_partition_pages(b, 8, t, num_cus=256, max_context=mc)
     assert plan(1, 128, 37) == 128  # 3 pages: no split
     assert plan(1, 128, 256) == 128  # 16 pages: no split
-    assert plan(1, 128, 257) == 16  # 17 pages: split
-    assert plan(1, 128, 2048) == 16
-    assert plan(17, 128, 856) == 16  # 54 pages over 4 partitions
-    assert plan(17, 128, 2048) == 32
-    assert plan(4, 128, 1024) == 16 and plan(8, 128, 1024) == 16
+    assert plan(1, 128, 384) == 128  # 24 pages: no split
+    assert plan(1, 128, 385) == 8  # 25 pages: split
+    assert plan(1, 128, 2048) == 8
+    assert plan(17, 128, 856) == 28  # 54 pages over 2 partitions
+    assert plan(17, 128, 2048) == 64
+    assert plan(4, 128, 1024) == 8 and plan(8, 128, 1024) == 16 and plan(16, 128, 1024) == 32
     assert plan(40, 128, 1024) == 128 and plan(40, 128, 2048) == 128
     assert plan(1, 300, 37) == 256  # the 256-page cap
     assert plan(256, 128, 2048) == 128
     for b in (1, 5, 16, 17, 40):
         assert plan(b, 128, None) == pkv.plan_partition_pages(b, 8, 128, num_cus=256)
     lib = pkv.library()
-    assert lib.pkv_plan_partition_pages_for_context(1, 8, 128, -1, 256) == 16
+    assert lib.pkv_plan_partition_pages_for_context(1, 8, 128, -1, 256) == 8
     assert lib.pkv_plan_partition_pages_for_context(1, 8, 128, 0, 256) == 128
-    assert lib.pkv_plan_partition_pages_for_context(1, 8, 128, 5000, 256) == 16  # clamped to the table
+    assert lib.pkv_plan_partition_pages_for_context(1, 8, 128, 5000, 256) == 8  # clamped to the table
     assert lib.pkv_plan_partition_pages_for_context(-1, 8, 128, 100, 256) == -1
 
 
