@@ -151,7 +151,10 @@ pkv_status pkv_rope_kv_append(const pkv_pool *pool, const int32_t *block_tables,
  * FP32 online softmax, gathering no contiguous prefix and storing no scores ("6 Hours of YouTube and 85 handtyped pages of notes on LLM Inference",
  * "What works so far"); the online-softmax merge of partial (max, sum) pairs is the rule of
  * "The prefill path: flowing the entire prompt at once", section "causalMask and online softmax".  Inputs are BF16,
- * all arithmetic is FP32, the output is FP32 or BF16 (round to nearest even).
+ * all arithmetic is FP32, the output is FP32 or BF16 (round to nearest even).  A NaN in a K row
+ * inside a sequence's context makes the 4 output rows of that KV group NaN, a NaN in a V row
+ * the dims it holds, split or not (as the definition gives); slot contents outside the context
+ * are never read into the result.
  *
  *   q                 device bf16[batch][num_q_heads][head_dim]
  *   k_pool, v_pool    device bf16[num_pages][num_kv_heads][block_size][head_dim]

@@ -246,7 +246,8 @@ constexpr int kMergeChunk = 16;
 // counter, and the partition that arrives last merges all of them with the pairwise (max, sum) rule
 // ("The prefill path: flowing the entire prompt at once", section "causalMask and online
 // softmax"): M* = max M_i, out = sum 2^(M_i - M*) O_i / sum 2^(M_i - M*) Ls_i, or zeros when a
-// partition marked itself invalid.  The merging partition reads the partials with swaps that
+// partition marked itself invalid (a NaN in a partition's keys or values reaches the output as it
+// does unsplit).  The merging partition reads the partials with swaps that
 // leave zeros behind and resets the counter, so the workspace is all-zero again when the launch
 // ends.  Swaps stand in for plain stores and loads because a device-scope atomic's round trip
 // (about 0.4 us on MI355X) is well under that of a device-coherent store's acknowledgement or a
@@ -321,7 +322,7 @@ __device__ __forceinline__ void finish_group(const DecodeParams &p, int b, int g
         const float e = __builtin_amdgcn_exp2f(mv[u] - Mc);
         Og = __builtin_fmaf(e, ov[u], Og);
         Lg = __builtin_fmaf(e, lv[u], Lg);
-        bad |= !(lv[u] >= 0.0f);
+        bad |= lv[u] < 0.0f;  // -1: an invalid table entry (a NaN sum propagates, as unsplit)
       }
     }
     Mg = Mc;

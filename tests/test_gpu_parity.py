@@ -571,3 +571,30 @@ def test_split_workspace_must_start_zeroed(gpu, monkeypatch):
     assert int(torch.count_nonzero(ws)) == 0
     ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens)
     assert_close(out.cpu().numpy(), ref, "zeroed workspace")
+
+
+@pytest.mark.parametrize("partition_pages", [0, 4, 8, 128])
+@pytest.mark.parametrize("row", ["k", "v"])
+def test_nan_inside_the_context_reaches_only_its_kv_group(gpu, partition_pages, row):
+    """A NaN K (or V) row at token 100 of sequence 4 (250 tokens, 16 pages), KV head 3: the
+    definition makes out[4, 12:16, :] NaN (every score of the group is NaN, or every weighted V row
+    is) and leaves every other row finite. Split into 4- or 8-page partitions the NaN K row leaves a
+    NaN denominator in one partition, which the merge must carry to the output instead of treating
+    the partition as one that met an invalid table entry (zeros); the planner's size (24 pages for
+    this 128-entry table) and 128 keep the sequence in one partition."""
+    w = make_custom(seed=27, lengths=[1, 7, 16, 17, 250, 1023], num_pages=120)
+    b, t, g = 4, 100, 3
+    page = int(w.block_tables[0, b, t // 16])
+    pool = w.k_pool if row == "k" else w.v_pool
+    pool[page, g, t % 16, :] = NAN_BITS
+    print(f"[attention] NaN {row} row inside the context, pp={partition_pages}", flush=True)
+    d = upload(w)
+    out = attend(gpu, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"],
+                 partition_pages=partition_pages).cpu().numpy()
+    ref = oracle.paged_decode_attention(w.q[0], w.k_pool, w.v_pool, w.block_tables[0], w.context_lens, 0.125)
+    expect = np.zeros(ref.shape, dtype=bool)
+    expect[b, 4 * g:4 * g + 4, :] = True
+    assert np.array_equal(np.isnan(ref), expect)  # the oracle's own reading of the definition
+    assert np.array_equal(np.isnan(out), expect)
+    keep = ~expect
+    assert_close(np.where(keep, out, 0.0), np.where(keep, ref, 0.0), f"NaN {row} row, pp={partition_pages}")
